@@ -1,0 +1,299 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's formula: they check page-printed worked
+examples (tests/golden), closed forms, finite differences, invariants and a
+library routine on the same inputs.
+"""
+import math
+
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import online_softmax as OS
+from oracle import sampled as SM
+from oracle import tiled as T
+from tests.conftest import read_golden
+
+F64 = torch.float64
+
+
+def rnd(shape, seed, scale=1.0):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=F64) * scale
+
+
+# --------------------------------------------------------------------------
+# online softmax: page-printed worked examples
+def test_online_softmax_blocks_match_page_example():
+    rows = read_golden("online_softmax_blocks.txt")
+    xs = [float(v) for v in rows[0][1:]]
+    block = int(rows[1][1])
+    states = [(int(r[1]), float(r[2]), float(r[3])) for r in rows if r[0] == "state"]
+    got = OS.blocks(xs, block)
+    assert len(got) == len(states)
+    for (n_read, m_ref, l_ref), (m, l) in zip(states, got):
+        assert m == pytest.approx(m_ref, abs=5e-7)
+        assert l == pytest.approx(l_ref, abs=5e-7), n_read
+    # final normaliser equals the whole-row sum (page: difference 0.0)
+    m_all = max(xs)
+    l_all = math.fsum(math.exp(x - m_all) for x in xs)
+    assert got[-1][0] == m_all
+    assert abs(got[-1][1] - l_all) <= 1e-15
+
+
+def test_online_softmax_stream_equals_blocks_and_direct():
+    xs = [float(v) for v in read_golden("online_softmax_blocks.txt")[0][1:]]
+    m, l = OS.stream(xs)
+    for b in (1, 2, 3, 5, 8):
+        mb, lb = OS.blocks(xs, b)[-1]
+        assert mb == m and abs(lb - l) <= 1e-15
+    p = OS.softmax_from_stats(xs, m, l)
+    direct = torch.softmax(torch.tensor(xs, dtype=F64), dim=0)
+    assert max(abs(a - b) for a, b in zip(p, direct.tolist())) <= 1e-16
+
+
+def test_merge_matches_page_exercise():
+    rows = {r[0]: r[1:] for r in read_golden("online_softmax_merge.txt")}
+    x1 = [float(v) for v in rows["part1"]]
+    x2 = [float(v) for v in rows["part2"]]
+    s1, s2 = OS.stream(x1), OS.stream(x2)
+    for got, key in ((s1, "state1"), (s2, "state2")):
+        assert got[0] == pytest.approx(float(rows[key][0]), abs=5e-7)
+        assert got[1] == pytest.approx(float(rows[key][1]), abs=5e-7)
+    mm = OS.merge(*s1, *s2)
+    assert mm[0] == pytest.approx(float(rows["merged"][0]), abs=5e-7)
+    assert mm[1] == pytest.approx(float(rows["merged"][1]), abs=5e-7)
+    # symmetric, and equal to reading the concatenated row directly
+    assert OS.merge(*s2, *s1) == pytest.approx(mm, abs=1e-15)
+    direct = OS.stream(x1 + x2)
+    assert direct == pytest.approx(mm, abs=1e-15)
+
+
+def test_merge_with_output_equals_whole_row_attention():
+    xs = rnd((13,), 7).tolist()
+    vs = rnd((13, 5), 8)
+    w = torch.softmax(torch.tensor(xs, dtype=F64), 0)
+    ref = (w.unsqueeze(1) * vs).sum(0)
+    cut = 6
+    parts = []
+    for lo, hi in ((0, cut), (cut, 13)):
+        m, l = OS.stream(xs[lo:hi])
+        p = torch.tensor([math.exp(x - m) / l for x in xs[lo:hi]], dtype=F64)
+        parts.append((m, l, (p.unsqueeze(1) * vs[lo:hi]).sum(0).tolist()))
+    m, l, o = OS.merge_with_output(*parts[0], *parts[1])
+    assert max(abs(a - b) for a, b in zip(o, ref.tolist())) <= 1e-15
+    # an empty part is the identity of the merge
+    assert OS.merge(-math.inf, 0.0, m, l) == (m, l)
+
+
+def test_safe_softmax_survives_overflowing_scores():
+    # exp(1000) overflows fp64 (the pages' example); the safe form does not
+    s = torch.tensor([[1000.0, 999.0, 998.0]], dtype=F64)
+    p, m, l = A.softmax_rows(s)
+    assert torch.isfinite(p).all() and m.item() == 1000.0
+    ref = torch.tensor([1.0, math.exp(-1), math.exp(-2)], dtype=F64)
+    assert torch.allclose(p[0], ref / ref.sum(), atol=1e-16, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# forward definition: closed forms, invariants, library cross-check
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_rows_sum_to_one(causal):
+    q, k = rnd((3, 40, 8), 1), rnd((3, 40, 8), 2)
+    p, _, _ = A.softmax_rows(A.scores(q, k, 0.7, causal))
+    assert torch.allclose(p.sum(-1), torch.ones(3, 40, dtype=F64), atol=1e-14, rtol=0)
+    if causal:
+        assert (p.triu(diagonal=1) == 0).all()
+
+
+def test_single_key_closed_form():
+    q, k, v, do = (rnd((2, 1, 4), s) for s in range(4))
+    o, lse = A.attention_forward(q, k, v, 0.3, False)
+    assert torch.equal(o, v)
+    assert torch.allclose(lse, 0.3 * (q * k).sum(-1), atol=1e-15, rtol=0)
+    dq, dk, dv = A.attention_backward(q, k, v, do, 0.3, False)
+    assert torch.equal(dv, do)
+    assert dq.abs().max() <= 1e-15 and dk.abs().max() <= 1e-15
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_queries_give_uniform_weights(causal):
+    n, d = 9, 4
+    q = torch.zeros(n, d, dtype=F64)
+    k, v = rnd((n, d), 3), rnd((n, d), 4)
+    o, lse = A.attention_forward(q, k, v, 1.0, causal)
+    if causal:
+        counts = torch.arange(1, n + 1, dtype=F64)
+        ref = v.cumsum(0) / counts.unsqueeze(1)
+        ref_lse = torch.log(counts)
+    else:
+        ref = v.mean(0).expand(n, d)
+        ref_lse = torch.full((n,), math.log(n), dtype=F64)
+    assert torch.allclose(o, ref, atol=1e-15, rtol=0)
+    assert torch.allclose(lse, ref_lse, atol=1e-15, rtol=0)
+
+
+def test_large_scale_selects_argmax_key():
+    q, k, v = rnd((6, 4), 5), rnd((11, 4), 6), rnd((11, 3), 7)
+    o, _ = A.attention_forward(q, k, v, 1e4, False)
+    idx = (q @ k.T).argmax(1)
+    assert torch.allclose(o, v[idx], atol=1e-9, rtol=0)
+
+
+def test_key_permutation_invariance():
+    q, k, v = rnd((7, 5), 8), rnd((12, 5), 9), rnd((12, 6), 10)
+    perm = torch.randperm(12, generator=torch.Generator().manual_seed(0))
+    o1, l1 = A.attention_forward(q, k, v, 0.5, False)
+    o2, l2 = A.attention_forward(q, k[perm], v[perm], 0.5, False)
+    assert torch.allclose(o1, o2, atol=1e-14, rtol=0) and torch.allclose(l1, l2, atol=1e-14, rtol=0)
+
+
+def test_causal_rows_ignore_future_keys():
+    n, d = 16, 4
+    q, k, v, do = (rnd((n, d), s) for s in range(20, 24))
+    o, lse = A.attention_forward(q, k, v, 0.8, True)
+    i0 = 6
+    k2, v2 = k.clone(), v.clone()
+    k2[i0 + 1:] += rnd((n - i0 - 1, d), 30)
+    v2[i0 + 1:] += rnd((n - i0 - 1, d), 31)
+    o2, lse2 = A.attention_forward(q, k2, v2, 0.8, True)
+    assert torch.equal(o[: i0 + 1], o2[: i0 + 1]) and torch.equal(lse[: i0 + 1], lse2[: i0 + 1])
+    # key j receives no gradient from queries i < j
+    do2 = do.clone()
+    do2[:i0] = 0.0
+    _, dk, dv = A.attention_backward(q, k, v, do, 0.8, True)
+    _, dk2, dv2 = A.attention_backward(q, k, v, do2, 0.8, True)
+    # dV_j depends only on dO_i for i >= j: rows j >= i0 unchanged
+    assert torch.allclose(dv[i0:], dv2[i0:], atol=1e-15, rtol=0)
+    assert torch.allclose(dk[i0:], dk2[i0:], atol=1e-15, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_library_sdpa_with_autograd(causal):
+    B, H, n, d = 2, 3, 37, 16
+    q, k, v, do = (rnd((B, H, n, d), s) for s in range(40, 44))
+    scale = 0.37
+    qa, ka, va = (t.clone().requires_grad_() for t in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(qa, ka, va, is_causal=causal, scale=scale)
+    ref.backward(do)
+    o, lse = A.attention_forward(q, k, v, scale, causal)
+    dq, dk, dv = A.attention_backward(q, k, v, do, scale, causal)
+    assert torch.allclose(o, ref.detach(), atol=1e-12, rtol=0)
+    for got, want in ((dq, qa.grad), (dk, ka.grad), (dv, va.grad)):
+        assert torch.allclose(got, want, atol=1e-12, rtol=0)
+    s = scale * q @ k.transpose(-1, -2)
+    if causal:
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    assert torch.allclose(lse, torch.logsumexp(s, -1), atol=1e-13, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# backward: finite differences and the D identity
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,d", [(1, 2), (5, 3), (8, 4)])
+def test_gradients_match_central_differences(causal, n, d):
+    q, k, v, do = (rnd((n, d), s) for s in (50 + n, 60 + n, 70 + n, 80 + n))
+    scale = 0.9
+
+    def loss(qq, kk, vv):
+        return float((A.attention_forward(qq, kk, vv, scale, causal)[0] * do).sum())
+
+    grads = A.attention_backward(q, k, v, do, scale, causal)
+    h = 1e-6
+    for which, g in enumerate(grads):
+        num = torch.zeros_like(g)
+        for idx in range(g.numel()):
+            args = [q.clone(), k.clone(), v.clone()]
+            args[which].view(-1)[idx] += h
+            up = loss(*args)
+            args[which].view(-1)[idx] -= 2 * h
+            dn = loss(*args)
+            num.view(-1)[idx] = (up - dn) / (2 * h)
+        denom = max(1.0, float(num.abs().max()))
+        assert float((num - g).abs().max()) / denom <= 1e-6, which
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_d_identity(causal):
+    q, k, v, do = (rnd((31, 8), s) for s in range(90, 94))
+    s = A.scores(q, k, 0.6, causal)
+    p, _, _ = A.softmax_rows(s)
+    o = p @ v
+    dp = do @ v.T
+    lhs = (p * dp).sum(-1)
+    rhs = (do * o).sum(-1)
+    assert torch.allclose(lhs, rhs, rtol=1e-13, atol=1e-13)
+
+
+def test_forward_backward_combined_equals_separate():
+    q, k, v, do = (rnd((2, 33, 8), s) for s in range(100, 104))
+    o, lse = A.attention_forward(q, k, v, 0.4, True)
+    g = A.attention_backward(q, k, v, do, 0.4, True)
+    both = A.attention_forward_backward(q, k, v, do, 0.4, True)
+    for a, b in zip((o, lse, *g), both):
+        assert torch.equal(a, b)
+
+
+def test_per_head_slicing_changes_nothing():
+    q, k, v, do = (rnd((2, 3, 17, 8), s) for s in range(110, 114))
+    full = A.attention_forward_backward(q, k, v, do, 0.4, True)
+    sliced = A.per_head(A.attention_forward_backward, (q, k, v, do), 0.4, True, heads_per_chunk=2)
+    for a, b in zip(full, sliced):
+        assert a.shape == b.shape and torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# sampled rows agree with the full oracle
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_equal_full(causal):
+    n, d = 300, 16
+    q, k, v, do = (rnd((n, d), s) for s in range(120, 124))
+    o, lse, dq, dk, dv = A.attention_forward_backward(q, k, v, do, 0.25, causal)
+    rows = torch.tensor([0, 1, 5, 127, 128, 299])
+    so, slse, sdq = SM.query_rows(q, k, v, do, rows, 0.25, causal)
+    assert torch.allclose(so, o[rows], atol=1e-13, rtol=0)
+    assert torch.allclose(slse, lse[rows], atol=1e-13, rtol=0)
+    assert torch.allclose(sdq, dq[rows], atol=1e-13, rtol=0)
+    cols = torch.tensor([0, 3, 64, 150, 298, 299])
+    sdk, sdv = SM.key_rows(q, k, v, do, cols, 0.25, causal, chunk=64)
+    assert torch.allclose(sdk, dk[cols], atol=1e-13, rtol=0)
+    assert torch.allclose(sdv, dv[cols], atol=1e-13, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# tiled models equal the whole-matrix definition (pages: 1e-16 .. 1e-15)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("blk", [16, 32, 64, 128])
+def test_tiled_forward_equals_standard(causal, blk):
+    n, d = 256, 32
+    q, k, v = (rnd((n, d), s) for s in range(130, 133))
+    o_ref, lse_ref = A.attention_forward(q, k, v, 1 / math.sqrt(d), causal)
+    o1, m1, l1 = T.forward_outer_kv(q, k, v, 1 / math.sqrt(d), causal, blk, blk)
+    assert float((o1 - o_ref).abs().max()) < 1e-14
+    assert float((m1 + torch.log(l1) - lse_ref).abs().max()) < 1e-14
+    o2, lse2 = T.forward_outer_q(q, k, v, 1 / math.sqrt(d), causal, blk, blk)
+    assert float((o2 - o_ref).abs().max()) < 1e-14
+    assert float((lse2 - lse_ref).abs().max()) < 1e-14
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiled_backward_equals_standard(causal):
+    n, d = 200, 16  # ragged: 200 is not a multiple of 64
+    q, k, v, do = (rnd((n, d), s) for s in range(140, 144))
+    o, lse = A.attention_forward(q, k, v, 0.3, causal)
+    ref = A.attention_backward(q, k, v, do, 0.3, causal)
+    got = T.backward_recompute(q, k, v, o, do, lse, 0.3, causal, 64, 48)
+    for a, b in zip(got, ref):
+        assert float((a - b).abs().max()) < 1e-13
+
+
+def test_causal_block_skipping_counts_page_example():
+    rows = [r for r in read_golden("io_counts.txt") if r[0] == "causal_blocks"][0]
+    nblk, needed = int(rows[1]), int(rows[2])
+    n, d = 256, 32
+    q, k, v = (rnd((n, d), s) for s in range(150, 153))
+    io = T.IOCount()
+    T.forward_outer_kv(q, k, v, 0.2, True, n // nblk, n // nblk, io)
+    assert io.pairs == needed
+    assert round(needed / nblk**2, 3) == float(rows[3])
