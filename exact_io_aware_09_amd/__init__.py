@@ -1,0 +1,16 @@
+"""Exact multi-head attention for AMD Instinct MI355X (gfx950).
+
+The product is the C-ABI shared library ``libfa_mi355x.so`` (declared in
+``include/fa.h``) built from the HIP kernels in ``csrc/``.  This package holds
+its ctypes binding (``_lib``: the C entry points under the same names), thin
+tensor wrappers (``attention.forward`` / ``attention.backward``) and the
+seeded synthetic workloads (``workloads``).
+"""
+from ._lib import (FA_BF16, FA_F32, FAError, fa_backward, fa_backward_workspace_bytes,  # noqa: F401
+                   fa_forward, fa_strerror, fa_version)
+from .attention import backward, forward, workspace_bytes  # noqa: F401
+
+__all__ = [
+    "FA_BF16", "FA_F32", "FAError", "fa_forward", "fa_backward", "fa_backward_workspace_bytes",
+    "fa_strerror", "fa_version", "forward", "backward", "workspace_bytes",
+]

@@ -1,0 +1,94 @@
+"""ctypes binding of ``libfa_mi355x.so`` (the C ABI in ``include/fa.h``).
+
+The functions here carry the same names as the C entry points and only
+marshal arguments: every step of the computation runs in the HIP kernels.
+If the shared library has not been built, loading fails loudly; there is no
+fallback path of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().parent / "libfa_mi355x.so"
+
+FA_BF16 = 0
+FA_F32 = 1
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_MISALIGNED = -3
+FA_ERR_NO_WORKSPACE = -4
+FA_ERR_HIP = -5
+
+# name -> (restype, argtypes); the single source for the exported symbol list
+_VP = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "fa_version": (_I, []),
+    "fa_strerror": (ctypes.c_char_p, [_I]),
+    "fa_forward": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _F, _I, _I, _VP]),
+    "fa_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "fa_backward": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
+                         _I, _I, _I, _I, _F, _I, _I, _VP]),
+}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-zero return code from the C ABI."""
+
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: error {code}: {fa_strerror(code)}")
+
+
+def load(path: str | os.PathLike | None = None) -> ctypes.CDLL:
+    """Load the shared library once and declare its signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(
+            f"{p} is not built; run `python -m exact_io_aware_09_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(str(p))
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def fa_version() -> int:
+    return int(load().fa_version())
+
+
+def fa_strerror(code: int) -> str:
+    return load().fa_strerror(int(code)).decode()
+
+
+def fa_forward(Q, K, V, O, LSE, B, H, N, d, scale, causal, dtype, stream) -> int:
+    """Raw call: device pointers as ints, returns the C return code."""
+    return int(load().fa_forward(Q, K, V, O, LSE, B, H, N, d, float(scale), int(causal),
+                                 int(dtype), stream))
+
+
+def fa_backward_workspace_bytes(B, H, N, d, dtype) -> int:
+    return int(load().fa_backward_workspace_bytes(B, H, N, d, int(dtype)))
+
+
+def fa_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H, N, d,
+                scale, causal, dtype, stream) -> int:
+    """Raw call: device pointers as ints, returns the C return code."""
+    return int(load().fa_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace,
+                                  workspace_bytes, B, H, N, d, float(scale), int(causal),
+                                  int(dtype), stream))

@@ -1,0 +1,101 @@
+// fa_api.hip -- the C ABI declared in include/fa.h: argument validation,
+// dispatch on (dtype, d, causal) and kernel launches.  Nothing here
+// allocates, frees or synchronises; everything is enqueued on the caller's
+// stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_sizes(int B, int H, int N, int d, int dtype) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  // Per-head offsets are 32-bit inside the kernels; the B*H*N row count and
+  // every grid must also stay below 2^31.
+  if ((long long)N * d > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * N > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int check_common(int B, int H, int N, int d, float scale, int causal, int dtype) {
+  const int rc = check_sizes(B, H, N, d, dtype);
+  if (rc != FA_OK) return rc;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return kVersion; }
+
+const char* fa_strerror(int code) {
+  switch (code) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size, scale not finite and > 0, causal not 0/1)";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration (d must be 64, 128 or 256; dtype FA_BF16 or FA_F32; sizes below 2^31)";
+    case FA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case FA_ERR_NO_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_bytes()";
+    case FA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+               int N, int d, float scale, int causal, int dtype, void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = (dtype == FA_BF16)
+                     ? fa::launch_forward_bf16(Q, K, V, O, LSE, p, s)
+                     : fa::launch_forward_f32((const float*)Q, (const float*)K, (const float*)V,
+                                              (float*)O, LSE, p, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  if (check_sizes(B, H, N, d, dtype) != FA_OK) return 0;
+  const size_t bytes = (size_t)B * H * N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                const float* LSE, void* dQ, void* dK, void* dV, void* workspace,
+                size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                int dtype, void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d, dtype))
+    return FA_ERR_NO_WORKSPACE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) ||
+      !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* Dws = static_cast<float*>(workspace);
+  hipError_t e =
+      (dtype == FA_BF16)
+          ? fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, s)
+          : fa::launch_backward_f32((const float*)Q, (const float*)K, (const float*)V,
+                                    (const float*)O, (const float*)dO, LSE, (float*)dQ,
+                                    (float*)dK, (float*)dV, Dws, p, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

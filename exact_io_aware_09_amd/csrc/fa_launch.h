@@ -1,0 +1,27 @@
+// fa_launch.h -- host-side launchers behind the C ABI (internal, C++ linkage).
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+struct Problem {
+  int B, H, N, d;
+  float scale;
+  bool causal;
+};
+
+// bfloat16 inputs, fp32 accumulation on the matrix cores.
+hipError_t launch_forward_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               const Problem& p, hipStream_t stream);
+hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
+                                const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                                float* Dws, const Problem& p, hipStream_t stream);
+
+// float32 throughout (vector ALU).
+hipError_t launch_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
+                              const Problem& p, hipStream_t stream);
+hipError_t launch_backward_f32(const float* Q, const float* K, const float* V, const float* O,
+                               const float* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                               float* Dws, const Problem& p, hipStream_t stream);
+
+}  // namespace fa

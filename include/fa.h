@@ -1,0 +1,106 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library.
+ *
+ * What is computed (per batch b and head h, all N x d matrices row-major):
+ *
+ *   S   = scale * Q K^T                      (N x N, never stored)
+ *   S_ij = -inf for j > i  when causal       (key j visible to query i iff j <= i)
+ *   P   = softmax over each row of S         (never stored)
+ *   O   = P V
+ *   LSE_i = ln sum_j exp(S_ij)               (natural log, scaled + masked scores)
+ *
+ * This is standard attention as defined in "Lecture 8 . GPU Performance &
+ * FlashAttention" (CS324 notes), section 5.1; the forward is computed tile by
+ * tile with the online softmax of section 5.2 of those notes ("FlashAttention
+ * and GPU memory", sections 07-08), so that only O and the per-row LSE reach
+ * device memory.  The backward recomputes S and P tile by tile from Q, K and
+ * LSE (CS324 notes section 5.4; "FlashAttention and GPU memory" section 09)
+ * and returns the gradients of L = sum(dO * O):
+ *
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_k dO_ik O_ik,
+ *   dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * Conventions shared by every entry point
+ * --------------------------------------
+ *  - Q, K, V, O, dO, dQ, dK, dV: contiguous [B, H, N, d] tensors of one
+ *    element type (`dtype`): FA_BF16 (bfloat16, fp32 accumulation inside)
+ *    or FA_F32 (float32 throughout).  LSE: contiguous float32 [B, H, N].
+ *  - All pointers are DEVICE pointers, 16-byte aligned.  The caller owns
+ *    every buffer; the library never allocates, frees or synchronises.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is only enqueued; functions return once it is enqueued.
+ *  - d must be 64, 128 or 256.  N >= 1 (any value; tails are masked),
+ *    B >= 1, H >= 1, B*H*N*d must fit in 2^31 - 1 elements.
+ *  - `scale` must be finite; `causal` is 0 or 1.
+ *  - Errors are returned as codes (never thrown across the ABI); argument
+ *    checks happen before anything is enqueued, so an error return means
+ *    nothing was launched (except FA_ERR_HIP, reported by the launch itself).
+ *  - No global mutable state: calls from several host threads are safe.
+ *    Calls that write the same output buffers on different streams race,
+ *    as any two kernels would.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
+
+enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive size, non-finite scale, causal not 0/1 */
+  FA_ERR_UNSUPPORTED = -2,  /* d not in {64,128,256}, unknown dtype, tensor too large */
+  FA_ERR_MISALIGNED = -3,   /* a pointer is not 16-byte aligned */
+  FA_ERR_NO_WORKSPACE = -4, /* workspace NULL or smaller than fa_backward_workspace_bytes() */
+  FA_ERR_HIP = -5           /* a kernel launch reported an error */
+};
+
+/* Library version as an integer (major*10000 + minor*100 + patch). */
+int fa_version(void);
+
+/* Human-readable text for a return code; never NULL. */
+const char* fa_strerror(int code);
+
+/*
+ * Forward pass.  Reads Q, K, V; writes O ([B,H,N,d], dtype) and LSE
+ * ([B,H,N] float32, natural log).  Tiles Q into row blocks and streams K/V
+ * blocks through on-chip memory with a running max / sum per row (CS324
+ * notes sections 5.2-5.3, in the loop order of section 8.1's second
+ * version: one Q block per workgroup, inner loop over K/V blocks).
+ */
+int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
+               int B, int H, int N, int d, float scale, int causal, int dtype,
+               void* stream);
+
+/*
+ * Bytes of device workspace fa_backward needs: one float32 per query row
+ * (the D vector of CS324 notes section 5.4), rounded up to 256 bytes.
+ * Returns 0 for invalid sizes.
+ */
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward pass.  Reads Q, K, V, O, dO and the forward's LSE; writes dQ, dK,
+ * dV (all [B,H,N,d], dtype) completely (no accumulation into the caller's
+ * buffers).  `workspace` (device memory of at least
+ * fa_backward_workspace_bytes(), contents ignored on entry) receives D.
+ * Three kernels are enqueued on `stream`, in order: D = rowsum(dO * O); a
+ * dK/dV kernel (one K/V block per workgroup, loop over Q blocks); a dQ
+ * kernel (one Q block per workgroup, loop over K/V blocks).  No atomics:
+ * results are bitwise reproducible run to run.
+ */
+int fa_backward(const void* Q, const void* K, const void* V, const void* O,
+                const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                void* workspace, size_t workspace_bytes,
+                int B, int H, int N, int d, float scale, int causal, int dtype,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

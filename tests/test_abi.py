@@ -1,0 +1,99 @@
+"""The C-ABI library loads without a GPU and exports what include/fa.h declares.
+
+Only calls that the library rejects during argument validation (before any
+HIP call) are made here; compute calls need a GPU and live in test_gpu_*.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import exact_io_aware_09_amd as fa
+from exact_io_aware_09_amd import _lib
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "fa.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    assert {"fa_forward", "fa_backward", "fa_backward_workspace_bytes", "fa_strerror",
+            "fa_version"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(_lib.LIB_PATH))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # the binding declares a signature for each of them
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_version_and_strerror():
+    assert fa.fa_version() >= 100
+    for code in (0, -1, -2, -3, -4, -5, 12345):
+        assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
+
+
+A = 1 << 20  # a 16-byte aligned fake address; never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(B=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(N=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(H=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(d=48), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=512), _lib.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.125), _lib.FA_ERR_INVALID_ARG),
+    (dict(causal=2), _lib.FA_ERR_INVALID_ARG),
+    (dict(Q=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(LSE=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(K=A + 2), _lib.FA_ERR_MISALIGNED),
+    (dict(LSE=A + 4), _lib.FA_ERR_MISALIGNED),
+    (dict(N=1 << 26, d=64), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_forward_validation(args, code):
+    kw = dict(Q=A, K=A, V=A, O=A, LSE=A, B=1, H=1, N=128, d=64, scale=0.125, causal=0,
+              dtype=_lib.FA_BF16, stream=None)
+    kw.update(args)
+    assert fa.fa_forward(**kw) == code
+
+
+def test_workspace_bytes():
+    assert fa.fa_backward_workspace_bytes(64, 16, 1024, 64, 0) == 64 * 16 * 1024 * 4
+    assert fa.fa_backward_workspace_bytes(1, 1, 1, 64, 0) == 256
+    assert fa.fa_backward_workspace_bytes(1, 1, 0, 64, 0) == 0
+    assert fa.fa_backward_workspace_bytes(1, 1, 8, 96, 0) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(workspace=0), _lib.FA_ERR_NO_WORKSPACE),
+    (dict(workspace_bytes=255), _lib.FA_ERR_NO_WORKSPACE),
+    (dict(dO=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(dV=A + 8), _lib.FA_ERR_MISALIGNED),
+    (dict(workspace=A + 8), _lib.FA_ERR_MISALIGNED),
+    (dict(d=32), _lib.FA_ERR_UNSUPPORTED),
+    (dict(causal=-1), _lib.FA_ERR_INVALID_ARG),
+])
+def test_backward_validation(args, code):
+    kw = dict(Q=A, K=A, V=A, O=A, dO=A, LSE=A, dQ=A, dK=A, dV=A, workspace=A,
+              workspace_bytes=256, B=1, H=1, N=16, d=64, scale=0.125, causal=1,
+              dtype=_lib.FA_BF16, stream=None)
+    kw.update(args)
+    assert fa.fa_backward(**kw) == code
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load(tmp_path / "nope.so")

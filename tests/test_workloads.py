@@ -1,0 +1,44 @@
+"""Seeded synthetic inputs: deterministic, right shapes, dtypes and rounding."""
+import numpy as np
+import torch
+
+from exact_io_aware_09_amd import workloads as W
+
+
+def test_same_seed_same_tensors():
+    a = W.make_inputs((1, 2, 33, 64), torch.bfloat16, 5)
+    b = W.make_inputs((1, 2, 33, 64), torch.bfloat16, 5)
+    for x, y in zip(a, b):
+        assert x.dtype == torch.bfloat16 and x.shape == (1, 2, 33, 64)
+        assert torch.equal(x, y)
+    c = W.make_inputs((1, 2, 33, 64), torch.bfloat16, 6)
+    assert not torch.equal(a[0], c[0])
+
+
+def test_draw_order_and_rounding():
+    g = torch.Generator("cpu").manual_seed(9)
+    raw = [torch.randn((2, 8), generator=g) for _ in range(4)]
+    got = W.make_inputs((2, 8), torch.bfloat16, 9, mult=0.5)
+    for r, x in zip(raw, got):
+        assert torch.equal((r * 0.5).to(torch.bfloat16), x)
+
+
+def test_workload_table():
+    assert set(W.WORKLOADS) == {"tiny", "gpt2_medium", "memory", "long", "big_d"}
+    g = W.WORKLOADS["gpt2_medium"]
+    assert (g.B, g.H, g.N, g.d, g.causal, g.scale) == (64, 16, 1024, 64, True, 0.125)
+    assert W.WORKLOADS["tiny"].dtype == torch.float32
+    assert W.WORKLOADS["big_d"].mult == 0.5 and W.WORKLOADS["big_d"].scale == 1 / 16
+
+
+def test_sample_rows_distinct_sorted_with_edges():
+    qi, ki = W.sample_rows(3, 0, 5, 8, 65536)
+    for idx in (qi, ki):
+        assert np.all(np.diff(idx) > 0)
+        assert idx.min() == 0 and idx.max() == 65535
+        assert {1, 127, 128, 255, 256} <= set(idx.tolist())
+        assert len(idx) >= 256
+    qi2, _ = W.sample_rows(3, 0, 5, 8, 65536)
+    assert np.array_equal(qi, qi2)
+    small_q, _ = W.sample_rows(0, 0, 0, 1, 10)
+    assert small_q.tolist() == list(range(10))
