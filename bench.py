@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Throughput of exact attention forward + backward on one MI355X.
+
+One step = fa_forward followed by the three backward stages (D
+preprocess, dK/dV, dQ -- exactly what fa_backward enqueues) over one batch of
+synthetic input already resident in device memory.  Default workload: the
+GPT-2-medium attention shape (B 64, H 16, N 1024, d 64, bfloat16, causal,
+scale 1/8).
+
+Credited FLOPs: forward 4*B*H*N^2*d (halved when causal), backward 2.5x the
+forward.  Per-kernel durations come from HIP events recorded on the stream
+the kernels run on; the roofline object reports the dominant kernel's
+algorithmic work per launch divided by its average duration.  The CPU
+baseline times the fp64 oracle (S and P materialised) on a bounded sample of
+the same workload on this host's cores.
+
+Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one
+GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+METRIC = "attention fwd+bwd TFLOP/s & % bf16 MFMA peak (B64 H16 N1024 d64 causal)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic.json"
+KERNELS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_medium")
+    ap.add_argument("--fwd-only", action="store_true", help="time only the forward kernel")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args(argv)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = ROOT / "exact_io_aware_09_amd" / "csrc"
+    for p in sorted(csrc.glob("*")):
+        if p.suffix in (".hip", ".h"):
+            h.update(p.name.encode())
+            h.update(p.read_bytes())
+    return h.hexdigest()
+
+
+def visible_pairs(w) -> int:
+    """(query, key) pairs that contribute, over all heads."""
+    per_head = w.N * (w.N + 1) // 2 if w.causal else w.N * w.N
+    return w.B * w.H * per_head
+
+
+def credited_flops(w):
+    fwd = 4 * w.B * w.H * w.N * w.N * w.d
+    if w.causal:
+        fwd //= 2
+    return fwd, fwd * 5 // 2
+
+
+def algorithmic(w, kernel, elem_bytes):
+    """(bound, amount per launch, unit) for each kernel.
+
+    Matrix-core work counts 2*d FLOPs per visible (query, key) pair per
+    contraction: forward 2 (Q K^T, P V), dK/dV 4 (Q K^T, dO V^T, P^T dO,
+    dS^T Q), dQ 3 (Q K^T, dO V^T, dS K).  The D preprocess is a streaming
+    pass: it reads O and dO once and writes one float per row.
+    """
+    e = elem_bytes
+    pairs = visible_pairs(w)
+    if kernel == "fwd":
+        return "mfma", 2 * 2 * w.d * pairs, "FLOP"
+    if kernel == "bwd_dkdv":
+        return "mfma", 4 * 2 * w.d * pairs, "FLOP"
+    if kernel == "bwd_dq":
+        return "mfma", 3 * 2 * w.d * pairs, "FLOP"
+    rows = w.B * w.H * w.N
+    return "hbm", 2 * rows * w.d * e + 4 * rows, "B"
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counters, if still valid."""
+    try:
+        data = json.loads(TRAFFIC_FILE.read_text())
+    except (OSError, ValueError):
+        return None
+    if data.get("source_sha256") != source_digest() or data.get("workload") != workload:
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return int(k["fetch_bytes"]) + int(k["write_bytes"])
+
+
+def cpu_baseline(w, seconds: float):
+    """Time the fp64 oracle on the first heads of the same workload."""
+    import torch
+
+    from exact_io_aware_09_amd.workloads import make_inputs
+    from oracle import attention as A  # the baseline is the oracle itself
+
+    # the workload's own inputs (same seed), flattened to heads
+    q, k, v, do = (t.reshape(w.B * w.H, w.N, w.d) for t in make_inputs(w.shape, w.dtype, w.seed, w.mult))
+    heads_done, t_used = 0, 0.0
+    chunk = 8
+    while t_used < seconds and heads_done < w.B * w.H:
+        sl = slice(heads_done, min(w.B * w.H, heads_done + chunk))
+        t0 = time.perf_counter()
+        A.per_head(A.attention_forward_backward, (q[sl], k[sl], v[sl], do[sl]),
+                   w.scale, w.causal, heads_per_chunk=chunk)
+        t_used += time.perf_counter() - t0
+        heads_done += sl.stop - sl.start
+    fwd, bwd = credited_flops(w)
+    per_head = (fwd + bwd) / (w.B * w.H)
+    tflops = per_head * heads_done / t_used / 1e12
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "cores": torch.get_num_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle forward+backward (S, P materialised) on {heads_done} heads "
+                   f"(N={w.N}, d={w.d}, causal={w.causal}) of the {w.name} workload's "
+                   f"{w.B * w.H}; {t_used:.1f} s; credited FLOPs of those heads / time"),
+    }
+
+
+def calibrate_copy():
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "launches": 3}), flush=True)
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the attention kernels run on one "
+              "GPU's share of heads); --gpus must be 1.", file=sys.stderr)
+        return 2
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    if args.calibrate_copy:
+        calibrate_copy()
+        return 0
+
+    import exact_io_aware_09_amd as fa
+    from exact_io_aware_09_amd import _lib
+    from exact_io_aware_09_amd.workloads import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    dtype_name = "bf16" if w.dtype == torch.bfloat16 else "f32"
+    dt = _lib.FA_BF16 if dtype_name == "bf16" else _lib.FA_F32
+    dev = torch.device("cuda:0")
+    B, H, N, d = w.shape
+
+    q, k, v, do = (t.to(dev) for t in workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    wsb = fa.workspace_bytes(B, H, N, d, w.dtype)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    P = [t.data_ptr() for t in (q, k, v, o, lse, do, dq, dk, dv, ws)]
+
+    def call(rc, name):
+        if rc != _lib.FA_OK:
+            raise fa.FAError(rc, name)
+
+    def launches(ev=None):
+        """One step; if `ev` is given, record events between the kernels."""
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        rec(0)
+        call(_lib.fa_forward(P[0], P[1], P[2], P[3], P[4], B, H, N, d, w.scale, int(w.causal),
+                             dt, sp), "fa_forward")
+        rec(1)
+        if args.fwd_only:
+            return
+        call(_lib.fa_backward_preprocess(P[3], P[5], P[9], wsb, B, H, N, d, dt, sp),
+             "fa_backward_preprocess")
+        rec(2)
+        call(_lib.fa_backward_dkdv(P[0], P[1], P[2], P[5], P[4], P[9], wsb, P[7], P[8], B, H, N,
+                                   d, w.scale, int(w.causal), dt, sp), "fa_backward_dkdv")
+        rec(3)
+        call(_lib.fa_backward_dq(P[0], P[1], P[2], P[5], P[4], P[9], wsb, P[6], B, H, N, d,
+                                 w.scale, int(w.causal), dt, sp), "fa_backward_dq")
+        rec(4)
+
+    for _ in range(args.warmup):
+        launches()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+
+    nev = 2 if args.fwd_only else 5
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        launches(evs[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    names = KERNELS[: nev - 1]
+    per_kernel = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                  for i, n in enumerate(names)}
+
+    fwd_fl, bwd_fl = credited_flops(w)
+    total_fl = fwd_fl if args.fwd_only else fwd_fl + bwd_fl
+    tflops = total_fl / (ms_step * 1e-3) / 1e12
+    dom = max(per_kernel, key=per_kernel.get)
+    bound, amount, _ = algorithmic(w, dom, 2 if dtype_name == "bf16" else 4)
+    dur_s = per_kernel[dom] * 1e-3
+    if bound == "mfma":
+        achieved, peak, unit = amount / dur_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = amount / dur_s / 1e9, PEAK_HBM_GBS, "GB/s"
+
+    result = {
+        "metric": METRIC if (args.workload == "gpt2_medium" and not args.fwd_only)
+        else f"attention {'fwd' if args.fwd_only else 'fwd+bwd'} TFLOP/s ({args.workload})",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "scale": w.scale, "input_dtype": dtype_name,
+                   "step": "forward" if args.fwd_only else "forward+backward"},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "peak_mem_bytes": torch.cuda.max_memory_allocated(dev),
+        "roofline": {
+            "kernel": dom,
+            "bound": bound,
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": stored_traffic(dom, w.name),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -18,9 +18,10 @@ int check_sizes(int B, int H, int N, int d, int dtype) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
-  // Per-head offsets are 32-bit inside the kernels; the B*H*N row count and
-  // every grid must also stay below 2^31.
-  if ((long long)N * d > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  // Per-head byte offsets are 32-bit inside the kernels (with room for one
+  // tail tile past the end); the B*H*N row count and every grid stay below
+  // 2^31.
+  if ((long long)N * d > 0x7fff0000LL) return FA_ERR_UNSUPPORTED;
   if ((long long)B * H * N > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
@@ -91,10 +92,79 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
   float* Dws = static_cast<float*>(workspace);
   hipError_t e =
       (dtype == FA_BF16)
-          ? fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, s)
+          ? fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, fa::kStagesAll, s)
           : fa::launch_backward_f32((const float*)Q, (const float*)K, (const float*)V,
                                     (const float*)O, (const float*)dO, LSE, (float*)dQ,
-                                    (float*)dK, (float*)dV, Dws, p, s);
+                                    (float*)dK, (float*)dV, Dws, p, fa::kStagesAll, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_backward_preprocess(const void* O, const void* dO, void* workspace, size_t workspace_bytes,
+                           int B, int H, int N, int d, int dtype, void* stream) {
+  int rc = check_sizes(B, H, N, d, dtype);
+  if (rc != FA_OK) return rc;
+  if (!O || !dO) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d, dtype))
+    return FA_ERR_NO_WORKSPACE;
+  if (!aligned16(O) || !aligned16(dO) || !aligned16(workspace)) return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, 1.0f, false};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* Dws = static_cast<float*>(workspace);
+  hipError_t e = (dtype == FA_BF16)
+                     ? fa::launch_backward_bf16(nullptr, nullptr, nullptr, O, dO, nullptr, nullptr,
+                                                nullptr, nullptr, Dws, p, fa::kStagePre, s)
+                     : fa::launch_backward_f32(nullptr, nullptr, nullptr, (const float*)O,
+                                               (const float*)dO, nullptr, nullptr, nullptr,
+                                               nullptr, Dws, p, fa::kStagePre, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO,
+                     const float* LSE, const void* workspace, size_t workspace_bytes, void* dK,
+                     void* dV, int B, int H, int N, int d, float scale, int causal, int dtype,
+                     void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (!Q || !K || !V || !dO || !LSE || !dK || !dV) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d, dtype))
+    return FA_ERR_NO_WORKSPACE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(LSE) ||
+      !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* Dws = const_cast<float*>(static_cast<const float*>(workspace));
+  hipError_t e =
+      (dtype == FA_BF16)
+          ? fa::launch_backward_bf16(Q, K, V, nullptr, dO, LSE, nullptr, dK, dV, Dws, p,
+                                     fa::kStageDkDv, s)
+          : fa::launch_backward_f32((const float*)Q, (const float*)K, (const float*)V, nullptr,
+                                    (const float*)dO, LSE, nullptr, (float*)dK, (float*)dV, Dws, p,
+                                    fa::kStageDkDv, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_backward_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                   const void* workspace, size_t workspace_bytes, void* dQ, int B, int H, int N,
+                   int d, float scale, int causal, int dtype, void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (!Q || !K || !V || !dO || !LSE || !dQ) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d, dtype))
+    return FA_ERR_NO_WORKSPACE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(LSE) ||
+      !aligned16(dQ) || !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* Dws = const_cast<float*>(static_cast<const float*>(workspace));
+  hipError_t e =
+      (dtype == FA_BF16)
+          ? fa::launch_backward_bf16(Q, K, V, nullptr, dO, LSE, dQ, nullptr, nullptr, Dws, p,
+                                     fa::kStageDq, s)
+          : fa::launch_backward_f32((const float*)Q, (const float*)K, (const float*)V, nullptr,
+                                    (const float*)dO, LSE, (float*)dQ, nullptr, nullptr, Dws, p,
+                                    fa::kStageDq, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

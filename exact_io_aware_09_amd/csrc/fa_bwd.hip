@@ -58,37 +58,36 @@ void bwd_pre_bf16_kernel(const bf16_t* __restrict__ O, const bf16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Per wavefront: 32 keys.  Per iteration: a chunk of BQ = 32*QB
-// query rows in LDS, stored row-major (A operand of S = Q K^T and of
-// dP = dO V^T) and transposed (A operand of dK^T += Q^T dS, dV^T += dO^T P).
-template <int D, int QB>
+// dK, dV.  Per wavefront: 32 keys whose K and V fragments stay in VGPRs.  Per
+// iteration: a chunk of BQ = 32*QB query rows of Q and dO staged in LDS
+// (swizzled, double-buffered), plus that chunk's LSE*log2(e) and D.  Q and
+// dO are read by rows for S = Q K^T and dP = dO V^T, and through the LDS
+// transpose unit for dK^T += Q^T dS and dV^T += dO^T P.
+template <int D, int NW, int QB>
 struct DkdvCfg {
-  static constexpr int NW = 4;
   static constexpr int NT = NW * kWave;
   static constexpr int BK = NW * 32;          // keys per workgroup
   static constexpr int BQ = 32 * QB;          // query rows per chunk
-  static constexpr int RS = D + 8;            // row-major stride (elements)
-  static constexpr int TS = BQ + 8;           // transposed stride (elements)
-  static constexpr int ROWT = BQ * RS;
-  static constexpr int TRT = D * TS;
-  // one buffer: Q, dO row-major; Q^T, dO^T; then LSE*log2e and D (floats)
-  static constexpr int BUF_ELEMS = 2 * ROWT + 2 * TRT + 2 * BQ * 2;
+  static constexpr int TILE = BQ * D;
+  // one buffer: Q tile, dO tile, then LSE*log2e and D (2*BQ floats)
+  static constexpr int BUF_ELEMS = 2 * TILE + 4 * BQ;
   static constexpr int CPR = D / 8;
   static constexpr int CPT = BQ * CPR / NT;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int PU = BQ / 16;
   static_assert(BQ * CPR % NT == 0, "chunk must split evenly over threads");
+  static_assert(BQ <= NT, "one thread per query row loads LSE and D");
 };
 
-template <int D, int QB, bool CAUSAL>
-__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2))
+template <int D, int NW, int QB, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, (D >= 128 ? 1 : 2))
 void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                           const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dws,
                           bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int BH, int N,
                           int nkb, float c, float scale) {
-  using C = DkdvCfg<D, QB>;
+  using C = DkdvCfg<D, NW, QB>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * C::BUF_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -97,10 +96,11 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   const int bh = L / nkb;
   const int kb = L % nkb;  // causal: low key blocks see the most queries, run them first
   const size_t hoff = (size_t)bh * N * D;
-  const bf16_t* Qh = Q + hoff;
-  const bf16_t* dOh = dO + hoff;
-  const float* Lh = LSE + (size_t)bh * N;
-  const float* Dh = Dws + (size_t)bh * N;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const auto rq = make_rsrc(Q + hoff, head_bytes);
+  const auto ro = make_rsrc(dO + hoff, head_bytes);
+  const auto rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
+  const auto rd = make_rsrc(Dws + (size_t)bh * N, (uint32_t)N * 4u);
 
   const int k0 = kb * C::BK;
   const int k0w = k0 + w * 32;
@@ -109,12 +109,13 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   // K and V fragments: B operands of S = Q K^T and dP = dO V^T (lane = key).
   bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
   {
-    const bool ok = key < N;
+    const auto rk = make_rsrc(K + hoff, head_bytes);
+    const auto rv = make_rsrc(V + hoff, head_bytes);
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
-      const size_t off = hoff + (size_t)key * D + 16 * s + 8 * h;
-      kf[s] = as_bf16x8(load16_or_zero(K + off, ok));
-      vf[s] = as_bf16x8(load16_or_zero(V + off, ok));
+      const uint32_t off = ((uint32_t)key * D + 16 * s + 8 * h) * 2u;
+      kf[s] = as_bf16x8(buf_load16(rk, off));
+      vf[s] = as_bf16x8(buf_load16(rv, off));
     }
   }
 
@@ -137,40 +138,25 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int chunk = tid + i * C::NT;
-      const int row = chunk / C::CPR, col = (chunk % C::CPR) * 8;
-      const bool ok = i0 + row < N;
-      const size_t off = (size_t)(i0 + row) * D + col;
-      qreg[i] = load16_or_zero(Qh + off, ok);
-      oreg[i] = load16_or_zero(dOh + off, ok);
+      const uint32_t off = ((uint32_t)(i0 + chunk / C::CPR) * D + (chunk % C::CPR) * 8) * 2u;
+      qreg[i] = buf_load16(rq, off);
+      oreg[i] = buf_load16(ro, off);
     }
     if (tid < C::BQ) {
-      const bool ok = i0 + tid < N;
-      lreg = ok ? Lh[i0 + tid] * kLog2e : 0.f;
-      dreg = ok ? Dh[i0 + tid] : 0.f;
+      lreg = buf_load_f32(rl, (uint32_t)(i0 + tid) * 4u) * kLog2e;
+      dreg = buf_load_f32(rd, (uint32_t)(i0 + tid) * 4u);
     }
   };
   auto lstore = [&](int buf) {
-    bf16_t* base = lds + buf * C::BUF_ELEMS;
-    bf16_t* Qs = base;
-    bf16_t* dOs = base + C::ROWT;
-    bf16_t* Qt = base + 2 * C::ROWT;
-    bf16_t* dOt = base + 2 * C::ROWT + C::TRT;
-    float* fl = reinterpret_cast<float*>(base + 2 * C::ROWT + 2 * C::TRT);
+    bf16_t* Qs = lds + buf * C::BUF_ELEMS;
+    bf16_t* Os = Qs + C::TILE;
+    float* fl = reinterpret_cast<float*>(Qs + 2 * C::TILE);
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int chunk = tid + i * C::NT;
-      const int row = chunk / C::CPR, col = (chunk % C::CPR) * 8;
-      *reinterpret_cast<uint4*>(Qs + row * C::RS + col) = qreg[i];
-      *reinterpret_cast<uint4*>(dOs + row * C::RS + col) = oreg[i];
-      const uint32_t qv[4] = {qreg[i].x, qreg[i].y, qreg[i].z, qreg[i].w};
-      const uint32_t ov[4] = {oreg[i].x, oreg[i].y, oreg[i].z, oreg[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Qt[(col + 2 * e) * C::TS + row] = (bf16_t)(qv[e] & 0xffffu);
-        Qt[(col + 2 * e + 1) * C::TS + row] = (bf16_t)(qv[e] >> 16);
-        dOt[(col + 2 * e) * C::TS + row] = (bf16_t)(ov[e] & 0xffffu);
-        dOt[(col + 2 * e + 1) * C::TS + row] = (bf16_t)(ov[e] >> 16);
-      }
+      const int off = tile_off<D>(chunk / C::CPR, (chunk % C::CPR) * 8);
+      *reinterpret_cast<uint4*>(Qs + off) = qreg[i];
+      *reinterpret_cast<uint4*>(Os + off) = oreg[i];
     }
     if (tid < C::BQ) {
       fl[tid] = lreg;
@@ -189,29 +175,26 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     // some query of the chunk sees some key of this wavefront
     const bool active = !CAUSAL || i0 + C::BQ - 1 >= k0w;
     if (active) {
-      const bf16_t* base = lds + buf * C::BUF_ELEMS;
-      const bf16_t* Qs = base;
-      const bf16_t* dOs = base + C::ROWT;
-      const bf16_t* Qt = base + 2 * C::ROWT;
-      const bf16_t* dOt = base + 2 * C::ROWT + C::TRT;
-      const float* fl = reinterpret_cast<const float*>(base + 2 * C::ROWT + 2 * C::TRT);
+      const bf16_t* Qs = lds + buf * C::BUF_ELEMS;
+      const bf16_t* Os = Qs + C::TILE;
+      const float* fl = reinterpret_cast<const float*>(Qs + 2 * C::TILE);
 
       // S = Q K^T and dP = dO V^T (lane: key; registers: query rows).
       f32x16 sacc[QB], pacc[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[qb][r] = 0.f;
-          pacc[qb][r] = 0.f;
-        }
-#pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
-          const int off = (qb * 32 + c32) * C::RS + 16 * s + 8 * h;
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qs + off);
-          const bf16x8 ao = *reinterpret_cast<const bf16x8*>(dOs + off);
-          sacc[qb] = mfma32x32x16(aq, kf[s], sacc[qb]);
-          pacc[qb] = mfma32x32x16(ao, vf[s], pacc[qb]);
+          const bf16x8 aq = frag_rows<D>(Qs, qb * 32, 16 * s, c32, h);
+          const bf16x8 ao = frag_rows<D>(Os, qb * 32, 16 * s, c32, h);
+          if (s == 0) {
+            const f32x16 z = {};
+            sacc[qb] = mfma32x32x16(aq, kf[s], z);
+            pacc[qb] = mfma32x32x16(ao, vf[s], z);
+          } else {
+            sacc[qb] = mfma32x32x16(aq, kf[s], sacc[qb]);
+            pacc[qb] = mfma32x32x16(ao, vf[s], pacc[qb]);
+          }
         }
       }
 
@@ -246,13 +229,8 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
         for (int u = 0; u < C::PU; ++u) {
-          const int off = (db * 32 + c32) * C::TS + 16 * u + 4 * h;
-          const bf16x4 olo = *reinterpret_cast<const bf16x4*>(dOt + off);
-          const bf16x4 ohi = *reinterpret_cast<const bf16x4*>(dOt + off + 8);
-          const bf16x4 qlo = *reinterpret_cast<const bf16x4*>(Qt + off);
-          const bf16x4 qhi = *reinterpret_cast<const bf16x4*>(Qt + off + 8);
-          const bf16x8 ao = __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 aq = __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 ao = frag_tr<D>(Os, 16 * u, db * 32, lane);
+          const bf16x8 aq = frag_tr<D>(Qs, 16 * u, db * 32, lane);
           dvacc[db] = mfma32x32x16(ao, pb[u], dvacc[db]);
           dkacc[db] = mfma32x32x16(aq, sb[u], dkacc[db]);
         }
@@ -283,20 +261,16 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// dQ.  Per wavefront: 32 query rows (Q and dO fragments in VGPRs).  Per
-// iteration: a block of BC keys in LDS: K and V row-major (A operands of
-// S^T = K Q^T and dP^T = V dO^T) and K transposed (A operand of
-// dQ^T += K^T dS^T).
-template <int D, int BC>
+// dQ.  Per wavefront: 32 query rows (Q and dO fragments in VGPRs, LSE and D
+// per lane).  Per iteration: a block of BC keys of K and V in LDS (swizzled,
+// double-buffered): K and V read by rows for S^T = K Q^T and dP^T = V dO^T,
+// K through the transpose unit for dQ^T += K^T dS^T.
+template <int D, int NW, int BC>
 struct DqCfg {
-  static constexpr int NW = 4;
   static constexpr int NT = NW * kWave;
   static constexpr int BR = NW * 32;
-  static constexpr int RS = D + 8;
-  static constexpr int TS = BC + 8;
-  static constexpr int ROWT = BC * RS;
-  static constexpr int TRT = D * TS;
-  static constexpr int BUF_ELEMS = 2 * ROWT + TRT;
+  static constexpr int TILE = BC * D;
+  static constexpr int BUF_ELEMS = 2 * TILE;
   static constexpr int CPR = D / 8;
   static constexpr int CPT = BC * CPR / NT;
   static constexpr int KSTEPS = D / 16;
@@ -306,13 +280,13 @@ struct DqCfg {
   static_assert(BC * CPR % NT == 0, "tile must split evenly over threads");
 };
 
-template <int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2))
+template <int D, int NW, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, (D >= 128 ? 1 : 2))
 void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                         const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ Dws,
                         bf16_t* __restrict__ dQ, int BH, int N, int nqb, float c, float scale) {
-  using C = DqCfg<D, BC>;
+  using C = DqCfg<D, NW, BC>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * C::BUF_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -321,23 +295,30 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
   const int bh = L / nqb;
   const int qb = CAUSAL ? (nqb - 1 - L % nqb) : (L % nqb);
   const size_t hoff = (size_t)bh * N * D;
-  const bf16_t* Kh = K + hoff;
-  const bf16_t* Vh = V + hoff;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const auto rk = make_rsrc(K + hoff, head_bytes);
+  const auto rv = make_rsrc(V + hoff, head_bytes);
 
   const int q0 = qb * C::BR;
   const int q0w = q0 + w * 32;
   const int query = q0w + c32;
-  const bool qok = query < N;
 
   bf16x8 qf[C::KSTEPS], of[C::KSTEPS];
+  float lse2, dd;
+  {
+    const auto rq = make_rsrc(Q + hoff, head_bytes);
+    const auto ro = make_rsrc(dO + hoff, head_bytes);
 #pragma unroll
-  for (int s = 0; s < C::KSTEPS; ++s) {
-    const size_t off = hoff + (size_t)query * D + 16 * s + 8 * h;
-    qf[s] = as_bf16x8(load16_or_zero(Q + off, qok));
-    of[s] = as_bf16x8(load16_or_zero(dO + off, qok));
+    for (int s = 0; s < C::KSTEPS; ++s) {
+      const uint32_t off = ((uint32_t)query * D + 16 * s + 8 * h) * 2u;
+      qf[s] = as_bf16x8(buf_load16(rq, off));
+      of[s] = as_bf16x8(buf_load16(ro, off));
+    }
+    const auto rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
+    const auto rd = make_rsrc(Dws + (size_t)bh * N, (uint32_t)N * 4u);
+    lse2 = buf_load_f32(rl, (uint32_t)query * 4u) * kLog2e;
+    dd = buf_load_f32(rd, (uint32_t)query * 4u);
   }
-  const float lse2 = qok ? LSE[(size_t)bh * N + query] * kLog2e : 0.f;
-  const float dd = qok ? Dws[(size_t)bh * N + query] : 0.f;
 
   f32x16 dqacc[C::DB];
 #pragma unroll
@@ -350,33 +331,23 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
 
   uint4 kreg[C::CPT], vreg[C::CPT];
   auto gload = [&](int t) {
-    const int j0 = t * BC;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int chunk = tid + i * C::NT;
-      const int row = chunk / C::CPR, col = (chunk % C::CPR) * 8;
-      const bool ok = j0 + row < N;
-      const size_t off = (size_t)(j0 + row) * D + col;
-      kreg[i] = load16_or_zero(Kh + off, ok);
-      vreg[i] = load16_or_zero(Vh + off, ok);
+      const uint32_t off = ((uint32_t)(t * BC + chunk / C::CPR) * D + (chunk % C::CPR) * 8) * 2u;
+      kreg[i] = buf_load16(rk, off);
+      vreg[i] = buf_load16(rv, off);
     }
   };
   auto lstore = [&](int buf) {
     bf16_t* Ks = lds + buf * C::BUF_ELEMS;
-    bf16_t* Vs = Ks + C::ROWT;
-    bf16_t* Kt = Ks + 2 * C::ROWT;
+    bf16_t* Vs = Ks + C::TILE;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int chunk = tid + i * C::NT;
-      const int row = chunk / C::CPR, col = (chunk % C::CPR) * 8;
-      *reinterpret_cast<uint4*>(Ks + row * C::RS + col) = kreg[i];
-      *reinterpret_cast<uint4*>(Vs + row * C::RS + col) = vreg[i];
-      const uint32_t kv[4] = {kreg[i].x, kreg[i].y, kreg[i].z, kreg[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Kt[(col + 2 * e) * C::TS + row] = (bf16_t)(kv[e] & 0xffffu);
-        Kt[(col + 2 * e + 1) * C::TS + row] = (bf16_t)(kv[e] >> 16);
-      }
+      const int off = tile_off<D>(chunk / C::CPR, (chunk % C::CPR) * 8);
+      *reinterpret_cast<uint4*>(Ks + off) = kreg[i];
+      *reinterpret_cast<uint4*>(Vs + off) = vreg[i];
     }
   };
 
@@ -391,25 +362,24 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
     const bool active = !CAUSAL || j0 <= q0w + 31;
     if (active) {
       const bf16_t* Ks = lds + buf * C::BUF_ELEMS;
-      const bf16_t* Vs = Ks + C::ROWT;
-      const bf16_t* Kt = Ks + 2 * C::ROWT;
+      const bf16_t* Vs = Ks + C::TILE;
 
       // S^T = K Q^T, dP^T = V dO^T (lane: query; registers: keys).
       f32x16 sacc[C::KB], pacc[C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[kb][r] = 0.f;
-          pacc[kb][r] = 0.f;
-        }
-#pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
-          const int off = (kb * 32 + c32) * C::RS + 16 * s + 8 * h;
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Ks + off);
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(Vs + off);
-          sacc[kb] = mfma32x32x16(ak, qf[s], sacc[kb]);
-          pacc[kb] = mfma32x32x16(av, of[s], pacc[kb]);
+          const bf16x8 ak = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
+          const bf16x8 av = frag_rows<D>(Vs, kb * 32, 16 * s, c32, h);
+          if (s == 0) {
+            const f32x16 z = {};
+            sacc[kb] = mfma32x32x16(ak, qf[s], z);
+            pacc[kb] = mfma32x32x16(av, of[s], z);
+          } else {
+            sacc[kb] = mfma32x32x16(ak, qf[s], sacc[kb]);
+            pacc[kb] = mfma32x32x16(av, of[s], pacc[kb]);
+          }
         }
       }
 
@@ -433,10 +403,7 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
       for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
         for (int u = 0; u < C::PU; ++u) {
-          const bf16_t* kp = Kt + (db * 32 + c32) * C::TS + 16 * u + 4 * h;
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(kp);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(kp + 8);
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 a = frag_tr<D>(Ks, 16 * u, db * 32, lane);
           dqacc[db] = mfma32x32x16(a, sb[u], dqacc[db]);
         }
       }
@@ -445,7 +412,7 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
     __syncthreads();
   }
 
-  if (qok) {
+  if (query < N) {
     bf16_t* dQr = dQ + hoff + (size_t)query * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -459,14 +426,14 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
   }
 }
 
-template <int D, int QB, int BC, bool CAUSAL>
+template <int D, int NWK, int QB, int NWQ, int BC, bool CAUSAL>
 hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                    const float* LSE, void* dQ, void* dK, void* dV, float* Dws, const Problem& p,
-                   hipStream_t stream) {
+                   unsigned stages, hipStream_t stream) {
   const int BH = p.B * p.H;
   const long long rows = (long long)BH * p.N;
   const float c = p.scale * kLog2e;
-  {
+  if (stages & kStagePre) {
     constexpr int RPB = 256 / (D / 8);
     const long long grid = (rows + RPB - 1) / RPB;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -475,45 +442,48 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
-    using C = DkdvCfg<D, QB>;
+  if (stages & kStageDkDv) {
+    using C = DkdvCfg<D, NWK, QB>;
     const int nkb = (p.N + C::BK - 1) / C::BK;
     const long long grid = (long long)BH * nkb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, QB, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, QB, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
                        stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                        (const bf16_t*)dO, LSE, Dws, (bf16_t*)dK, (bf16_t*)dV, BH, p.N, nkb, c,
                        p.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
-    using C = DqCfg<D, BC>;
+  if (stages & kStageDq) {
+    using C = DqCfg<D, NWQ, BC>;
     const int nqb = (p.N + C::BR - 1) / C::BR;
     const long long grid = (long long)BH * nqb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, BC, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, BC, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
                        stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                        (const bf16_t*)dO, LSE, Dws, (bf16_t*)dQ, BH, p.N, nqb, c, p.scale);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
-                                float* Dws, const Problem& p, hipStream_t stream) {
+                                float* Dws, const Problem& p, unsigned stages,
+                                hipStream_t stream) {
   switch (p.d) {
     case 64:
-      return p.causal ? run_bwd<64, 2, 64, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream)
-                      : run_bwd<64, 2, 64, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream);
+      return p.causal ? run_bwd<64, 4, 2, 4, 64, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream)
+                      : run_bwd<64, 4, 2, 4, 64, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
     case 128:
-      return p.causal ? run_bwd<128, 1, 64, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream)
-                      : run_bwd<128, 1, 64, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream);
+      return p.causal ? run_bwd<128, 4, 1, 4, 64, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream)
+                      : run_bwd<128, 4, 1, 4, 64, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
     case 256:
-      return p.causal ? run_bwd<256, 1, 32, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream)
-                      : run_bwd<256, 1, 32, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream);
+      return p.causal ? run_bwd<256, 4, 1, 4, 32, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream)
+                      : run_bwd<256, 4, 1, 4, 32, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
     default:
       return hipErrorInvalidValue;
   }

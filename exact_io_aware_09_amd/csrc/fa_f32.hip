@@ -263,24 +263,32 @@ hipError_t run_fwd_f32(const float* Q, const float* K, const float* V, float* O,
 template <int D, bool CAUSAL>
 hipError_t run_bwd_f32(const float* Q, const float* K, const float* V, const float* O,
                        const float* dO, const float* LSE, float* dQ, float* dK, float* dV,
-                       float* Dws, const Problem& p, hipStream_t stream) {
+                       float* Dws, const Problem& p, unsigned stages, hipStream_t stream) {
   constexpr int RPB = 256 / (D / 16);
   const long long rows = (long long)p.B * p.H * p.N;
   const long long gpre = (rows + RPB - 1) / RPB;
   const int nb = (p.N + RPB - 1) / RPB;
   const long long grid = (long long)p.B * p.H * nb;
   if (gpre > 0x7fffffffLL || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)gpre), dim3(256), 0, stream, O, dO,
-                     Dws, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     Q, K, V, dO, LSE, Dws, dK, dV, p.N, nb, p.scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, Q,
-                     K, V, dO, LSE, Dws, dQ, p.N, nb, p.scale);
-  return hipGetLastError();
+  if (stages & kStagePre) {
+    hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)gpre), dim3(256), 0, stream, O, dO,
+                       Dws, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kStageDkDv) {
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, Q, K, V, dO, LSE, Dws, dK, dV, p.N, nb, p.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kStageDq) {
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       Q, K, V, dO, LSE, Dws, dQ, p.N, nb, p.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -304,17 +312,18 @@ hipError_t launch_forward_f32(const float* Q, const float* K, const float* V, fl
 
 hipError_t launch_backward_f32(const float* Q, const float* K, const float* V, const float* O,
                                const float* dO, const float* LSE, float* dQ, float* dK, float* dV,
-                               float* Dws, const Problem& p, hipStream_t stream) {
+                               float* Dws, const Problem& p, unsigned stages,
+                               hipStream_t stream) {
   switch (p.d) {
     case 64:
-      return p.causal ? run_bwd_f32<64, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream)
-                      : run_bwd_f32<64, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream);
+      return p.causal ? run_bwd_f32<64, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream)
+                      : run_bwd_f32<64, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
     case 128:
-      return p.causal ? run_bwd_f32<128, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream)
-                      : run_bwd_f32<128, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream);
+      return p.causal ? run_bwd_f32<128, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream)
+                      : run_bwd_f32<128, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
     case 256:
-      return p.causal ? run_bwd_f32<256, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream)
-                      : run_bwd_f32<256, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stream);
+      return p.causal ? run_bwd_f32<256, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream)
+                      : run_bwd_f32<256, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
     default:
       return hipErrorInvalidValue;
   }

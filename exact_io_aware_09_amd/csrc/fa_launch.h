@@ -13,15 +13,18 @@ struct Problem {
 // bfloat16 inputs, fp32 accumulation on the matrix cores.
 hipError_t launch_forward_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                const Problem& p, hipStream_t stream);
+// Backward stages, enqueued in this order when several bits are set.
+enum : unsigned { kStagePre = 1u, kStageDkDv = 2u, kStageDq = 4u, kStagesAll = 7u };
+
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
-                                float* Dws, const Problem& p, hipStream_t stream);
+                                float* Dws, const Problem& p, unsigned stages, hipStream_t stream);
 
 // float32 throughout (vector ALU).
 hipError_t launch_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
                               const Problem& p, hipStream_t stream);
 hipError_t launch_backward_f32(const float* Q, const float* K, const float* V, const float* O,
                                const float* dO, const float* LSE, float* dQ, float* dK, float* dV,
-                               float* Dws, const Problem& p, hipStream_t stream);
+                               float* Dws, const Problem& p, unsigned stages, hipStream_t stream);
 
 }  // namespace fa

@@ -30,8 +30,9 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is only enqueued; functions return once it is enqueued.
  *  - d must be 64, 128 or 256.  N >= 1 (any value; tails are masked),
- *    B >= 1, H >= 1, B*H*N*d must fit in 2^31 - 1 elements.
- *  - `scale` must be finite; `causal` is 0 or 1.
+ *    B >= 1, H >= 1; N*d <= 2^31 - 2^16 and B*H*N < 2^31.
+ *  - `scale` must be finite and > 0 (the pages' scale is a positive factor,
+ *    1/sqrt(d) in practice); `causal` is 0 or 1.
  *  - Errors are returned as codes (never thrown across the ABI); argument
  *    checks happen before anything is enqueued, so an error return means
  *    nothing was launched (except FA_ERR_HIP, reported by the launch itself).
@@ -52,7 +53,7 @@ typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
 
 enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive size, non-finite scale, causal not 0/1 */
+  FA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive size, scale not finite and > 0, causal not 0/1 */
   FA_ERR_UNSUPPORTED = -2,  /* d not in {64,128,256}, unknown dtype, tensor too large */
   FA_ERR_MISALIGNED = -3,   /* a pointer is not 16-byte aligned */
   FA_ERR_NO_WORKSPACE = -4, /* workspace NULL or smaller than fa_backward_workspace_bytes() */
@@ -98,6 +99,31 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O,
                 void* workspace, size_t workspace_bytes,
                 int B, int H, int N, int d, float scale, int causal, int dtype,
                 void* stream);
+
+/*
+ * The three stages of fa_backward as separate calls, for callers that want
+ * to schedule or time them individually.  Enqueuing fa_backward_preprocess,
+ * fa_backward_dkdv and fa_backward_dq in that order on one stream computes
+ * exactly what fa_backward computes (the same kernels, bit for bit).
+ *
+ * fa_backward_preprocess: D_i = sum_k dO_ik O_ik (float32, natural
+ *   accumulation order of the kernel) into `workspace` -- the identity of
+ *   CS324 notes section 5.4 that replaces sum_j P_ij dP_ij.
+ * fa_backward_dkdv: reads Q, K, V, dO, LSE and D (workspace); writes dK, dV.
+ * fa_backward_dq:   reads Q, K, V, dO, LSE and D (workspace); writes dQ.
+ * Both later stages require D from fa_backward_preprocess on the same data.
+ */
+int fa_backward_preprocess(const void* O, const void* dO, void* workspace, size_t workspace_bytes,
+                           int B, int H, int N, int d, int dtype, void* stream);
+
+int fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO,
+                     const float* LSE, const void* workspace, size_t workspace_bytes,
+                     void* dK, void* dV, int B, int H, int N, int d, float scale, int causal,
+                     int dtype, void* stream);
+
+int fa_backward_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                   const void* workspace, size_t workspace_bytes, void* dQ, int B, int H, int N,
+                   int d, float scale, int causal, int dtype, void* stream);
 
 #ifdef __cplusplus
 }
