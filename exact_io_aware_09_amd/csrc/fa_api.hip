@@ -5,7 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_launch.h"
 
 namespace {

@@ -80,8 +80,8 @@ struct DkdvCfg {
   static_assert(BQ <= NT, "one thread per query row loads LSE and D");
 };
 
-template <int D, int NW, int QB, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, (D >= 128 ? 1 : 2))
+template <int D, int NW, int QB, int OCC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                           const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dws,
@@ -166,6 +166,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 
   gload(0);
   lstore(0);
+  wait_vmem_all();
   __syncthreads();
 
   for (int t = 0; t < nchunks; ++t) {
@@ -198,31 +199,48 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
         }
       }
 
-      const bool need_mask = (i0 + C::BQ > N) || (CAUSAL && i0 < k0w + 31);
-      bf16x8 pb[C::PU], sb[C::PU];
+      // P = exp2(S c - LSE2); masked entries (causal future, query tail) are
+      // zeroed on the blocks that need it only (a real branch).
+      float pv[QB][16];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          // rows 8g + 4h + 0..3 of this 32-row block: one 16-byte LDS read each
-          const int qi = qb * 32 + 8 * g + 4 * h;
-          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(fl + qi);
-          const f32x4 dd4 = *reinterpret_cast<const f32x4*>(fl + C::BQ + qi);
+          // rows 8g + 4h + 0..3 of this 32-row block: one 16-byte LDS read
+          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(fl + qb * 32 + 8 * g + 4 * h);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float p = fast_exp2(fmaf(sacc[qb][r], c, -lse4[e]));
-            if (need_mask) {
-              const int query = i0 + qi + e;
-              if (query >= N || (CAUSAL && key > query)) p = 0.f;
-            }
-            const float ds = p * (pacc[qb][r] - dd4[e]);
-            // k-step u = 2*qb + (g>>1), element 4*(g&1) + e
-            pb[2 * qb + (g >> 1)][4 * (g & 1) + e] = to_bf16(p);
-            sb[2 * qb + (g >> 1)][4 * (g & 1) + e] = to_bf16(ds);
-          }
+          for (int e = 0; e < 4; ++e) pv[qb][4 * g + e] = fast_exp2(fmaf(sacc[qb][4 * g + e], c, -lse4[e]));
         }
+      const bool need_mask = (i0 + C::BQ > N) || (CAUSAL && i0 < k0w + 31);
+      if (need_mask) {
+        keep_branch();
+        const int kqh = key - i0 - 4 * h;  // key > query  <=>  kqh > query offset
+        const int nq = N - i0 - 4 * h;     // query >= N  <=>  query offset >= nq
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
+            if ((CAUSAL && kqh > qoff) || qoff >= nq) pv[qb][r] = 0.f;
+          }
       }
+      // dS = P (dP - D); P and dS packed to bf16 as B operands (k-step
+      // u = 2*qb + (g>>1) holds registers 8*(g&1) .. of block qb).
+      uint32_t pw[C::PU][4], sw[C::PU][4];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 dd4 = *reinterpret_cast<const f32x4*>(fl + C::BQ + qb * 32 + 8 * g + 4 * h);
+          float ds[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[e] = pv[qb][4 * g + e] * (pacc[qb][4 * g + e] - dd4[e]);
+          const int u = 2 * qb + (g >> 1), w0 = 2 * (g & 1);
+          pw[u][w0] = pack_bf16x2(pv[qb][4 * g], pv[qb][4 * g + 1]);
+          pw[u][w0 + 1] = pack_bf16x2(pv[qb][4 * g + 2], pv[qb][4 * g + 3]);
+          sw[u][w0] = pack_bf16x2(ds[0], ds[1]);
+          sw[u][w0 + 1] = pack_bf16x2(ds[2], ds[3]);
+        }
 
       // dV^T += dO^T P,  dK^T += Q^T dS  (lane: key; registers: head dims).
 #pragma unroll
@@ -231,8 +249,8 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
         for (int u = 0; u < C::PU; ++u) {
           const bf16x8 ao = frag_tr<D>(Os, 16 * u, db * 32, lane);
           const bf16x8 aq = frag_tr<D>(Qs, 16 * u, db * 32, lane);
-          dvacc[db] = mfma32x32x16(ao, pb[u], dvacc[db]);
-          dkacc[db] = mfma32x32x16(aq, sb[u], dkacc[db]);
+          dvacc[db] = mfma32x32x16(ao, bf16x8_from(pw[u][0], pw[u][1], pw[u][2], pw[u][3]), dvacc[db]);
+          dkacc[db] = mfma32x32x16(aq, bf16x8_from(sw[u][0], sw[u][1], sw[u][2], sw[u][3]), dkacc[db]);
         }
       }
     }
@@ -280,8 +298,8 @@ struct DqCfg {
   static_assert(BC * CPR % NT == 0, "tile must split evenly over threads");
 };
 
-template <int D, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, (D >= 128 ? 1 : 2))
+template <int D, int NW, int BC, int OCC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                         const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ Dws,
@@ -353,6 +371,7 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
 
   gload(0);
   lstore(0);
+  wait_vmem_all();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -383,20 +402,35 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
         }
       }
 
-      const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
-      bf16x8 sb[C::PU];
+      // P^T = exp2(S^T c - LSE2); masked entries (causal future, key tail) are
+      // zeroed on the blocks that need it only (a real branch).
+      float pv[C::KB][16];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(sacc[kb][r], c, -lse2));
-          if (need_mask) {
-            const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key >= N || (CAUSAL && key > query)) p = 0.f;
+        for (int r = 0; r < 16; ++r) pv[kb][r] = fast_exp2(fmaf(sacc[kb][r], c, -lse2));
+      const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
+      if (need_mask) {
+        keep_branch();
+        const int kq = j0 + 4 * h - query;  // key - query = kq + key offset
+        const int nk = N - j0 - 4 * h;      // key >= N  <=>  key offset >= nk
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
+            if ((CAUSAL && kq + koff > 0) || koff >= nk) pv[kb][r] = 0.f;
           }
-          const float ds = p * (pacc[kb][r] - dd);
-          sb[2 * kb + (r >> 3)][r & 7] = to_bf16(ds);
-        }
+      }
+      // dS^T = P^T (dP^T - D), packed to bf16: register r of block kb is
+      // k-step 2*kb + (r>>3), element r & 7.
+      uint32_t sw[C::PU][4];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+          sw[2 * kb + (r >> 3)][(r & 7) >> 1] =
+              pack_bf16x2(pv[kb][r] * (pacc[kb][r] - dd), pv[kb][r + 1] * (pacc[kb][r + 1] - dd));
 
       // dQ^T += K^T dS^T (lane: query; registers: head dims).
 #pragma unroll
@@ -404,7 +438,7 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
 #pragma unroll
         for (int u = 0; u < C::PU; ++u) {
           const bf16x8 a = frag_tr<D>(Ks, 16 * u, db * 32, lane);
-          dqacc[db] = mfma32x32x16(a, sb[u], dqacc[db]);
+          dqacc[db] = mfma32x32x16(a, bf16x8_from(sw[u][0], sw[u][1], sw[u][2], sw[u][3]), dqacc[db]);
         }
       }
     }
@@ -426,7 +460,7 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
   }
 }
 
-template <int D, int NWK, int QB, int NWQ, int BC, bool CAUSAL>
+template <int D, int NWK, int QB, int OCCK, int NWQ, int BC, int OCCQ, bool CAUSAL>
 hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                    const float* LSE, void* dQ, void* dK, void* dV, float* Dws, const Problem& p,
                    unsigned stages, hipStream_t stream) {
@@ -447,7 +481,7 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
     const int nkb = (p.N + C::BK - 1) / C::BK;
     const long long grid = (long long)BH * nkb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, QB, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, QB, OCCK, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
                        stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                        (const bf16_t*)dO, LSE, Dws, (bf16_t*)dK, (bf16_t*)dV, BH, p.N, nkb, c,
                        p.scale);
@@ -459,13 +493,36 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
     const int nqb = (p.N + C::BR - 1) / C::BR;
     const long long grid = (long long)BH * nqb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, BC, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, BC, OCCQ, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
                        stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                        (const bf16_t*)dO, LSE, Dws, (bf16_t*)dQ, BH, p.N, nqb, c, p.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Launch configurations per head dim: dK/dV (wavefronts per workgroup,
+// 32-row query blocks per chunk, minimum wavefronts per SIMD), then dQ
+// (wavefronts per workgroup, keys per K/V block, minimum wavefronts per SIMD).
+#ifndef FA_BWD_CFG_D64
+#define FA_BWD_CFG_D64 4, 2, 2, 4, 64, 2
+#endif
+#ifndef FA_BWD_CFG_D128
+#define FA_BWD_CFG_D128 4, 1, 1, 4, 64, 1
+#endif
+#ifndef FA_BWD_CFG_D256
+#define FA_BWD_CFG_D256 4, 1, 1, 4, 32, 1
+#endif
+
+template <int D, int NWK, int QB, int OCCK, int NWQ, int BC, int OCCQ>
+hipError_t run_bwd_c(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* LSE, void* dQ, void* dK, void* dV, float* Dws, const Problem& p,
+                     unsigned stages, hipStream_t stream) {
+  return p.causal ? run_bwd<D, NWK, QB, OCCK, NWQ, BC, OCCQ, true>(Q, K, V, O, dO, LSE, dQ, dK, dV,
+                                                                  Dws, p, stages, stream)
+                  : run_bwd<D, NWK, QB, OCCK, NWQ, BC, OCCQ, false>(Q, K, V, O, dO, LSE, dQ, dK,
+                                                                   dV, Dws, p, stages, stream);
 }
 
 }  // namespace
@@ -476,14 +533,11 @@ hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, con
                                 hipStream_t stream) {
   switch (p.d) {
     case 64:
-      return p.causal ? run_bwd<64, 4, 2, 4, 64, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream)
-                      : run_bwd<64, 4, 2, 4, 64, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
+      return run_bwd_c<64, FA_BWD_CFG_D64>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
     case 128:
-      return p.causal ? run_bwd<128, 4, 1, 4, 64, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream)
-                      : run_bwd<128, 4, 1, 4, 64, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
+      return run_bwd_c<128, FA_BWD_CFG_D128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
     case 256:
-      return p.causal ? run_bwd<256, 4, 1, 4, 32, true>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream)
-                      : run_bwd<256, 4, 1, 4, 32, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
+      return run_bwd_c<256, FA_BWD_CFG_D256>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
     default:
       return hipErrorInvalidValue;
   }

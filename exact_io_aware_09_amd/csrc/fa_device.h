@@ -42,8 +42,53 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t u) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Exchange with the lane 32 positions away (the other half of the wave).
-__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+// Combine a value with the one held by the lane 32 positions away (the other
+// half of the wave) using v_permlane32_swap (a VALU op; no LDS round trip).
+// After swapping a register with a copy of itself, r[0] holds the low-half
+// value and r[1] the high-half value in every lane, so both halves compute
+// the same result from operands in the same order.
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// s_waitcnt vmcnt(0): every outstanding vector-memory load has landed.  Used
+// once before a main loop so that loads issued in the prologue (register
+// fragments) are not tracked into the loop, where the compiler would
+// otherwise wait on the in-order counter -- i.e. on the next block's
+// prefetch -- before each use.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int PER, int MAXT>
+__device__ __forceinline__ void wait_vmem_tiles(int tiles);
+
+// s_waitcnt vmcnt(N): at most N vector-memory loads of this wavefront still
+// outstanding (they complete in issue order).  N < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most `tiles` * PER loads are outstanding (tiles <= MAXT,
+// uniform across the wavefront); the immediate is selected by a switch.
+template <int PER, int MAXT>
+__device__ __forceinline__ void wait_vmem_tiles(int tiles) {
+  static_assert(MAXT <= 6, "extend the switch");
+  switch (tiles) {
+    case 0: wait_vmem_le<0>(); break;
+    case 1: wait_vmem_le<(1 <= MAXT ? PER : 0)>(); break;
+    case 2: wait_vmem_le<(2 <= MAXT ? 2 * PER : 0)>(); break;
+    case 3: wait_vmem_le<(3 <= MAXT ? 3 * PER : 0)>(); break;
+    case 4: wait_vmem_le<(4 <= MAXT ? 4 * PER : 0)>(); break;
+    case 5: wait_vmem_le<(5 <= MAXT ? 5 * PER : 0)>(); break;
+    default: wait_vmem_le<(6 <= MAXT ? 6 * PER : 0)>(); break;
+  }
+}
 
 // Workgroup -> logical tile index such that consecutive logical tiles land on
 // the same XCD.  Hardware hands workgroup w to XCD (w mod 8); a bijection
@@ -134,11 +179,60 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
 
+// Two fp32 values rounded (RNE) to bf16 and packed into one dword with a
+// single v_cvt_pk_bf16_f32; `a` lands in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ bf16x8 bf16x8_from(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16x8, make_uint4(a, b, c, d));
+}
+
+// Direct global -> LDS copy of one [ROWS x D] bf16 block (rows r0.. of the
+// buffer resource's tensor) into a swizzled LDS tile, without VGPRs.  Each
+// wavefront instruction writes 64 x 16 bytes to consecutive LDS addresses
+// (lane L at base + 16 L, base wave-uniform), so lane L fetches the global
+// chunk that the swizzle places at that position.  Rows past the end of the
+// resource read as zeros.  Completion is tracked by the vector-memory counter.
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, int r0, bf16_t* tile, int tid) {
+  constexpr int CPR = D / 8;               // chunks per row
+  constexpr int CHUNKS = ROWS * CPR;
+  constexpr int NWAVE = NT / kWave;
+  static_assert(CHUNKS % NT == 0, "block must split evenly over the threads");
+  typedef __attribute__((address_space(3))) void* lds_void_ptr;
+  const int w = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int i = 0; i < CHUNKS / NT; ++i) {
+    const int blk = w + i * NWAVE;           // 1 KB block of the tile written by this instruction
+    const int pos = blk * 64 + lane;         // chunk position in LDS
+    const int row = pos / CPR, c = (pos % CPR) ^ swz<D>(row);
+    const uint32_t goff = ((uint32_t)(r0 + row) * D + c * 8) * 2u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(tile + blk * 512), 16, goff, 0, 0, 0);
+  }
+}
+
+// Scheduling hints: ask the compiler's scheduler to interleave instruction
+// classes in the enclosing region (MFMA, transcendental, other VALU, LDS read).
+#define FA_SCHED_MFMA(n) __builtin_amdgcn_sched_group_barrier(0x008, (n), 0)
+#define FA_SCHED_VALU(n) __builtin_amdgcn_sched_group_barrier(0x002, (n), 0)
+#define FA_SCHED_TRANS(n) __builtin_amdgcn_sched_group_barrier(0x400, (n), 0)
+#define FA_SCHED_DSREAD(n) __builtin_amdgcn_sched_group_barrier(0x100, (n), 0)
+
 // Sum of the two bf16 products a.x*b.x + a.y*b.y accumulated into c (fp32).
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
 }
+
+// Keeps a rarely taken, wave-uniform block as a real branch: the compiler may
+// not execute an asm statement speculatively, so it cannot if-convert the
+// block into selects evaluated on every iteration.
+__device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
