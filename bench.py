@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of exact attention forward + backward on one MI355X.
 
-One step = fa_forward followed by the three backward stages (D
-preprocess, dK/dV, dQ -- exactly what fa_backward enqueues) over one batch of
-synthetic input already resident in device memory.  Default workload: the
+One step = fa_forward followed by the two backward stages (dQ, which also
+forms D = rowsum(dO * O), then dK/dV -- exactly what fa_backward enqueues)
+over one batch of synthetic input already resident in device memory.  Default workload: the
 GPT-2-medium attention shape (B 64, H 16, N 1024, d 64, bfloat16, causal,
 scale 1/8).
 
@@ -35,7 +35,7 @@ METRIC = "attention fwd+bwd TFLOP/s & % bf16 MFMA peak (B64 H16 N1024 d64 causal
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic.json"
-KERNELS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+KERNELS = ("fwd", "bwd_dq", "bwd_dkdv")
 
 
 def parse_args(argv=None):
@@ -81,8 +81,9 @@ def algorithmic(w, kernel, elem_bytes):
 
     Matrix-core work counts 2*d FLOPs per visible (query, key) pair per
     contraction: forward 2 (Q K^T, P V), dK/dV 4 (Q K^T, dO V^T, P^T dO,
-    dS^T Q), dQ 3 (Q K^T, dO V^T, dS K).  The D preprocess is a streaming
-    pass: it reads O and dO once and writes one float per row.
+    dS^T Q), dQ 3 (Q K^T, dO V^T, dS K).  The standalone D preprocess (not
+    part of a step) is a streaming pass: it reads O and dO once and writes
+    one float per row.
     """
     e = elem_bytes
     pairs = visible_pairs(w)
@@ -204,22 +205,19 @@ def main(argv=None):
         rec(1)
         if args.fwd_only:
             return
-        call(_lib.fa_backward_preprocess(P[3], P[5], P[9], wsb, B, H, N, d, dt, sp),
-             "fa_backward_preprocess")
+        call(_lib.fa_backward_dq(P[0], P[1], P[2], P[3], P[5], P[4], P[9], wsb, P[6], B, H, N,
+                                 d, w.scale, int(w.causal), dt, sp), "fa_backward_dq")
         rec(2)
         call(_lib.fa_backward_dkdv(P[0], P[1], P[2], P[5], P[4], P[9], wsb, P[7], P[8], B, H, N,
                                    d, w.scale, int(w.causal), dt, sp), "fa_backward_dkdv")
         rec(3)
-        call(_lib.fa_backward_dq(P[0], P[1], P[2], P[5], P[4], P[9], wsb, P[6], B, H, N, d,
-                                 w.scale, int(w.causal), dt, sp), "fa_backward_dq")
-        rec(4)
 
     for _ in range(args.warmup):
         launches()
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
 
-    nev = 2 if args.fwd_only else 5
+    nev = 2 if args.fwd_only else 4
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

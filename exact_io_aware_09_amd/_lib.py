@@ -38,7 +38,7 @@ SIGNATURES = {
     "fa_backward_preprocess": (_I, [_VP, _VP, _VP, _SZ, _I, _I, _I, _I, _I, _VP]),
     "fa_backward_dkdv": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP,
                               _I, _I, _I, _I, _F, _I, _I, _VP]),
-    "fa_backward_dq": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP,
+    "fa_backward_dq": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP,
                             _I, _I, _I, _I, _F, _I, _I, _VP]),
 }
 
@@ -110,7 +110,7 @@ def fa_backward_dkdv(Q, K, V, dO, LSE, workspace, workspace_bytes, dK, dV, B, H,
                                        B, H, N, d, float(scale), int(causal), int(dtype), stream))
 
 
-def fa_backward_dq(Q, K, V, dO, LSE, workspace, workspace_bytes, dQ, B, H, N, d, scale, causal,
-                   dtype, stream) -> int:
-    return int(load().fa_backward_dq(Q, K, V, dO, LSE, workspace, workspace_bytes, dQ,
+def fa_backward_dq(Q, K, V, O, dO, LSE, workspace, workspace_bytes, dQ, B, H, N, d, scale,
+                   causal, dtype, stream) -> int:
+    return int(load().fa_backward_dq(Q, K, V, O, dO, LSE, workspace, workspace_bytes, dQ,
                                      B, H, N, d, float(scale), int(causal), int(dtype), stream))

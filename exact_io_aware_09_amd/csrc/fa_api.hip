@@ -92,10 +92,10 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
   float* Dws = static_cast<float*>(workspace);
   hipError_t e =
       (dtype == FA_BF16)
-          ? fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, fa::kStagesAll, s)
+          ? fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, fa::kStagesGrad, s)
           : fa::launch_backward_f32((const float*)Q, (const float*)K, (const float*)V,
                                     (const float*)O, (const float*)dO, LSE, (float*)dQ,
-                                    (float*)dK, (float*)dV, Dws, p, fa::kStagesAll, s);
+                                    (float*)dK, (float*)dV, Dws, p, fa::kStagesGrad, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -144,27 +144,27 @@ int fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_backward_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                   const void* workspace, size_t workspace_bytes, void* dQ, int B, int H, int N,
-                   int d, float scale, int causal, int dtype, void* stream) {
+int fa_backward_dq(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* LSE, void* workspace, size_t workspace_bytes, void* dQ, int B,
+                   int H, int N, int d, float scale, int causal, int dtype, void* stream) {
   int rc = check_common(B, H, N, d, scale, causal, dtype);
   if (rc != FA_OK) return rc;
-  if (!Q || !K || !V || !dO || !LSE || !dQ) return FA_ERR_INVALID_ARG;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ) return FA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d, dtype))
     return FA_ERR_NO_WORKSPACE;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(LSE) ||
-      !aligned16(dQ) || !aligned16(workspace))
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(LSE) || !aligned16(dQ) || !aligned16(workspace))
     return FA_ERR_MISALIGNED;
   const fa::Problem p{B, H, N, d, scale, causal != 0};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  float* Dws = const_cast<float*>(static_cast<const float*>(workspace));
+  float* Dws = static_cast<float*>(workspace);
   hipError_t e =
       (dtype == FA_BF16)
-          ? fa::launch_backward_bf16(Q, K, V, nullptr, dO, LSE, dQ, nullptr, nullptr, Dws, p,
+          ? fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, nullptr, nullptr, Dws, p,
                                      fa::kStageDq, s)
-          : fa::launch_backward_f32((const float*)Q, (const float*)K, (const float*)V, nullptr,
-                                    (const float*)dO, LSE, (float*)dQ, nullptr, nullptr, Dws, p,
-                                    fa::kStageDq, s);
+          : fa::launch_backward_f32((const float*)Q, (const float*)K, (const float*)V,
+                                    (const float*)O, (const float*)dO, LSE, (float*)dQ, nullptr,
+                                    nullptr, Dws, p, fa::kStageDq, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

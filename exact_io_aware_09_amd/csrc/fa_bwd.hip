@@ -12,12 +12,15 @@
 // needs only N x d data.
 //
 // Three kernels, no atomics (results are bitwise reproducible):
-//   pre   D = rowsum(dO * O), fp32, bandwidth-bound.
+//   dq    one block of 128 query rows per workgroup (32 per wavefront),
+//         loop over K/V blocks staged in LDS; dQ written once.  It also
+//         forms D for its rows from the O and dO fragments it holds and
+//         stores D for the next kernel.
 //   dkdv  one block of 128 keys per workgroup (32 per wavefront, K and V
 //         fragments held in VGPRs), loop over query chunks staged in LDS;
 //         dK and dV accumulate in registers and are written once.
-//   dq    one block of 128 query rows per workgroup (32 per wavefront),
-//         loop over K/V blocks staged in LDS; dQ written once.
+//   pre   D = rowsum(dO * O) alone, fp32, bandwidth-bound; only for callers
+//         that run the dK/dV stage without the dQ stage.
 // Matrix-core orientation is chosen per kernel so that the operand that is
 // reused stays in registers, softmax statistics are per-lane where possible,
 // and the P / dS fragments produced by one v_mfma_f32_32x32x16_bf16 are fed
@@ -86,15 +89,14 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
                           const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Dws,
                           bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int BH, int N,
-                          int nkb, float c, float scale) {
+                          int nkb, int G, float c, float scale) {
   using C = DkdvCfg<D, NW, QB>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * C::BUF_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
-  const int L = xcd_remap(blockIdx.x, BH * nkb);
-  const int bh = L / nkb;
-  const int kb = L % nkb;  // causal: low key blocks see the most queries, run them first
+  int bh, kb;  // causal: low key blocks see the most queries, run them first
+  grouped_order(xcd_remap(blockIdx.x, BH * nkb), nkb, BH, G, bh, kb);
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rq = make_rsrc(Q + hoff, head_bytes);
@@ -280,7 +282,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 
 // ---------------------------------------------------------------------------
 // dQ.  Per wavefront: 32 query rows (Q and dO fragments in VGPRs, LSE and D
-// per lane).  Per iteration: a block of BC keys of K and V in LDS (swizzled,
+// per lane; D is formed here and stored for the dK/dV kernel).  Per iteration: a block of BC keys of K and V in LDS (swizzled,
 // double-buffered): K and V read by rows for S^T = K Q^T and dP^T = V dO^T,
 // K through the transpose unit for dQ^T += K^T dS^T.
 template <int D, int NW, int BC>
@@ -301,17 +303,18 @@ struct DqCfg {
 template <int D, int NW, int BC, int OCC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
-                        const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
-                        const float* __restrict__ LSE, const float* __restrict__ Dws,
-                        bf16_t* __restrict__ dQ, int BH, int N, int nqb, float c, float scale) {
+                        const bf16_t* __restrict__ V, const bf16_t* __restrict__ O,
+                        const bf16_t* __restrict__ dO, const float* __restrict__ LSE,
+                        float* __restrict__ Dws, bf16_t* __restrict__ dQ, int BH, int N, int nqb,
+                        int G, float c, float scale) {
   using C = DqCfg<D, NW, BC>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * C::BUF_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
-  const int L = xcd_remap(blockIdx.x, BH * nqb);
-  const int bh = L / nqb;
-  const int qb = CAUSAL ? (nqb - 1 - L % nqb) : (L % nqb);
+  int bh, rank;
+  grouped_order(xcd_remap(blockIdx.x, BH * nqb), nqb, BH, G, bh, rank);
+  const int qb = CAUSAL ? (nqb - 1 - rank) : rank;  // longest causal blocks first
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rk = make_rsrc(K + hoff, head_bytes);
@@ -321,21 +324,32 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
   const int q0w = q0 + w * 32;
   const int query = q0w + c32;
 
+  // Q and dO fragments (B operands, lane = query row: half h holds head dims
+  // 16s + 8h .. +7), LSE in log2 units, and D_i = sum_k dO_ik O_ik formed
+  // here from the matching O fragment and stored for the dK/dV kernel.
   bf16x8 qf[C::KSTEPS], of[C::KSTEPS];
   float lse2, dd;
   {
     const auto rq = make_rsrc(Q + hoff, head_bytes);
     const auto ro = make_rsrc(dO + hoff, head_bytes);
+    const auto rO = make_rsrc(O + hoff, head_bytes);
+    bf16x8 ov[C::KSTEPS];
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
       const uint32_t off = ((uint32_t)query * D + 16 * s + 8 * h) * 2u;
       qf[s] = as_bf16x8(buf_load16(rq, off));
       of[s] = as_bf16x8(buf_load16(ro, off));
+      ov[s] = as_bf16x8(buf_load16(rO, off));
     }
     const auto rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
-    const auto rd = make_rsrc(Dws + (size_t)bh * N, (uint32_t)N * 4u);
     lse2 = buf_load_f32(rl, (uint32_t)query * 4u) * kLog2e;
-    dd = buf_load_f32(rd, (uint32_t)query * 4u);
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)of[s][e], (float)ov[s][e], part);
+    dd = sum_halves(part);
+    if (h == 0 && query < N) Dws[(size_t)bh * N + query] = dd;
   }
 
   f32x16 dqacc[C::DB];
@@ -476,26 +490,29 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stages & kStageDkDv) {
-    using C = DkdvCfg<D, NWK, QB>;
-    const int nkb = (p.N + C::BK - 1) / C::BK;
-    const long long grid = (long long)BH * nkb;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, QB, OCCK, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
-                       stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                       (const bf16_t*)dO, LSE, Dws, (bf16_t*)dK, (bf16_t*)dV, BH, p.N, nkb, c,
-                       p.scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   if (stages & kStageDq) {
     using C = DqCfg<D, NWQ, BC>;
     const int nqb = (p.N + C::BR - 1) / C::BR;
     const long long grid = (long long)BH * nqb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int G = head_group(OCCQ * 4 / NWQ, nqb);
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, BC, OCCQ, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
                        stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                       (const bf16_t*)dO, LSE, Dws, (bf16_t*)dQ, BH, p.N, nqb, c, p.scale);
+                       (const bf16_t*)O, (const bf16_t*)dO, LSE, Dws, (bf16_t*)dQ, BH, p.N, nqb, G,
+                       c, p.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kStageDkDv) {
+    using C = DkdvCfg<D, NWK, QB>;
+    const int nkb = (p.N + C::BK - 1) / C::BK;
+    const long long grid = (long long)BH * nkb;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int G = head_group(OCCK * 4 / NWK, nkb);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, QB, OCCK, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
+                       stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                       (const bf16_t*)dO, LSE, Dws, (bf16_t*)dK, (bf16_t*)dV, BH, p.N, nkb, G, c,
+                       p.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -26,6 +26,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kCusPerXcd = 32;
+
+// Heads per group for grouped_order: about one XCD's worth of resident
+// workgroups (wgs_per_cu of them on each of its CUs) per group.
+constexpr int head_group(int wgs_per_cu, int nblk) {
+  const int slots = kCusPerXcd * (wgs_per_cu > 0 ? wgs_per_cu : 1);
+  return slots / nblk > 0 ? slots / nblk : 1;
+}
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -98,6 +106,21 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   const int q = total / kNumXcd, r = total % kNumXcd;
   const int x = w % kNumXcd, idx = w / kNumXcd;
   return x * q + (x < r ? x : r) + idx;
+}
+
+// Logical tile index -> (head, rank) for launches of nblk blocks per head
+// whose lengths differ (causal): heads are taken in groups of G, and inside a
+// group every head's rank-0 block comes first, then every rank-1 block, and
+// so on.  Rank 0 is the longest block.  With G * nblk close to the number of
+// workgroups one XCD holds at once, each XCD starts its long blocks first
+// (short tail at the end of the launch) while the K/V (or Q/dO) of only G
+// heads are live in its L2.  The last group may hold fewer than G heads.
+__device__ __forceinline__ void grouped_order(int L, int nblk, int BH, int G, int& bh, int& rank) {
+  const int per = G * nblk;
+  const int g = L / per, r = L - g * per;
+  const int gh = min(G, BH - g * G);
+  bh = g * G + r % gh;
+  rank = r / gh;
 }
 
 // 16-byte global load returning zeros when `ok` is false.

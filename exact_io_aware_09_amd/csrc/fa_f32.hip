@@ -270,21 +270,23 @@ hipError_t run_bwd_f32(const float* Q, const float* K, const float* V, const flo
   const int nb = (p.N + RPB - 1) / RPB;
   const long long grid = (long long)p.B * p.H * nb;
   if (gpre > 0x7fffffffLL || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (stages & kStagePre) {
+  // the dQ stage forms D itself (here with the standalone kernel) and leaves
+  // it in the workspace for the dK/dV stage
+  if (stages & (kStagePre | kStageDq)) {
     hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)gpre), dim3(256), 0, stream, O, dO,
                        Dws, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (stages & kStageDkDv) {
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, Q, K, V, dO, LSE, Dws, dK, dV, p.N, nb, p.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kStageDq) {
     hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream,
                        Q, K, V, dO, LSE, Dws, dQ, p.N, nb, p.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kStageDkDv) {
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, Q, K, V, dO, LSE, Dws, dK, dV, p.N, nb, p.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -33,7 +33,8 @@
 //    the same base).  Rows decide individually, so each row's arithmetic
 //    depends on its own scores alone.
 //  * Workgroups are remapped so that all query blocks of a head run on one
-//    XCD (shared L2 for the re-read K/V), longest causal blocks first.
+//    XCD (shared L2 for the re-read K/V); within a group of heads that fills
+//    an XCD, the longest causal blocks of every head start first.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -63,7 +64,7 @@ template <int D, int NW, int BC, int ST, int OCC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, OCC)
 void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      const bf16_t* __restrict__ V, bf16_t* __restrict__ O,
-                     float* __restrict__ LSE, int BH, int N, int nqb, float c) {
+                     float* __restrict__ LSE, int BH, int N, int nqb, int G, float c) {
   using C = FwdCfg<D, NW, BC, ST>;
   __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_ELEMS];
   auto kst = [&](int i) { return lds + (2 * i) * C::TILE; };
@@ -71,9 +72,9 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
-  const int L = xcd_remap(blockIdx.x, BH * nqb);
-  const int bh = L / nqb;
-  const int qb = CAUSAL ? (nqb - 1 - L % nqb) : (L % nqb);
+  int bh, rank;
+  grouped_order(xcd_remap(blockIdx.x, BH * nqb), nqb, BH, G, bh, rank);
+  const int qb = CAUSAL ? (nqb - 1 - rank) : rank;  // longest causal blocks first
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rq = make_rsrc(Q + hoff, head_bytes);
@@ -220,9 +221,10 @@ hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* 
   const long long grid = (long long)BH * nqb;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = p.scale * kLog2e;
+  const int G = head_group(OCC * 4 / NW, nqb);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid), dim3(C::NT),
                      0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O,
-                     LSE, BH, p.N, nqb, c);
+                     LSE, BH, p.N, nqb, G, c);
   return hipGetLastError();
 }
 

@@ -13,8 +13,11 @@ struct Problem {
 // bfloat16 inputs, fp32 accumulation on the matrix cores.
 hipError_t launch_forward_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                const Problem& p, hipStream_t stream);
-// Backward stages, enqueued in this order when several bits are set.
-enum : unsigned { kStagePre = 1u, kStageDkDv = 2u, kStageDq = 4u, kStagesAll = 7u };
+// Backward stages, enqueued in this order when several bits are set:
+//   kStagePre   D = rowsum(dO * O) into the workspace;
+//   kStageDq    dQ; also forms D from O and dO and stores it in the workspace;
+//   kStageDkDv  dK, dV; reads D from the workspace.
+enum : unsigned { kStagePre = 1u, kStageDq = 2u, kStageDkDv = 4u, kStagesGrad = 6u };
 
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,

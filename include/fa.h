@@ -89,9 +89,10 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype);
  * dV (all [B,H,N,d], dtype) completely (no accumulation into the caller's
  * buffers).  `workspace` (device memory of at least
  * fa_backward_workspace_bytes(), contents ignored on entry) receives D.
- * Three kernels are enqueued on `stream`, in order: D = rowsum(dO * O); a
- * dK/dV kernel (one K/V block per workgroup, loop over Q blocks); a dQ
- * kernel (one Q block per workgroup, loop over K/V blocks).  No atomics:
+ * Two kernels are enqueued on `stream`, in order: a dQ kernel (one Q block
+ * per workgroup, loop over K/V blocks) that also forms D = rowsum(dO * O)
+ * for its rows and stores it in `workspace`; then a dK/dV kernel (one K/V
+ * block per workgroup, loop over Q blocks) that reads D.  No atomics:
  * results are bitwise reproducible run to run.
  */
 int fa_backward(const void* Q, const void* K, const void* V, const void* O,
@@ -101,29 +102,34 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O,
                 void* stream);
 
 /*
- * The three stages of fa_backward as separate calls, for callers that want
- * to schedule or time them individually.  Enqueuing fa_backward_preprocess,
- * fa_backward_dkdv and fa_backward_dq in that order on one stream computes
- * exactly what fa_backward computes (the same kernels, bit for bit).
+ * The stages of fa_backward as separate calls, for callers that want to
+ * schedule or time them individually.  Enqueuing fa_backward_dq and then
+ * fa_backward_dkdv on one stream computes exactly what fa_backward computes
+ * (the same kernels, bit for bit).
  *
- * fa_backward_preprocess: D_i = sum_k dO_ik O_ik (float32, natural
- *   accumulation order of the kernel) into `workspace` -- the identity of
- *   CS324 notes section 5.4 that replaces sum_j P_ij dP_ij.
+ * fa_backward_dq:   reads Q, K, V, O, dO and LSE; writes dQ, and writes D
+ *   (D_i = sum_k dO_ik O_ik, float32: the identity of CS324 notes section
+ *   5.4 that replaces sum_j P_ij dP_ij) into `workspace`.
  * fa_backward_dkdv: reads Q, K, V, dO, LSE and D (workspace); writes dK, dV.
- * fa_backward_dq:   reads Q, K, V, dO, LSE and D (workspace); writes dQ.
- * Both later stages require D from fa_backward_preprocess on the same data.
+ *   D must come from fa_backward_dq or fa_backward_preprocess on the same
+ *   O and dO, enqueued earlier.
+ * fa_backward_preprocess: D alone into `workspace` (a streaming pass over O
+ *   and dO), for callers that run fa_backward_dkdv without fa_backward_dq.
+ *   Its D may differ from fa_backward_dq's in the last bits (different
+ *   summation order).
+ * Errors and argument rules are those of fa_backward.
  */
 int fa_backward_preprocess(const void* O, const void* dO, void* workspace, size_t workspace_bytes,
                            int B, int H, int N, int d, int dtype, void* stream);
+
+int fa_backward_dq(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* LSE, void* workspace, size_t workspace_bytes, void* dQ, int B,
+                   int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 int fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO,
                      const float* LSE, const void* workspace, size_t workspace_bytes,
                      void* dK, void* dV, int B, int H, int N, int d, float scale, int causal,
                      int dtype, void* stream);
-
-int fa_backward_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                   const void* workspace, size_t workspace_bytes, void* dQ, int B, int H, int N,
-                   int d, float scale, int causal, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -304,3 +304,38 @@ def test_long_sequence_allocates_nothing_quadratic():
     free1, _ = torch.cuda.mem_get_info()
     assert torch.cuda.max_memory_allocated() == base
     assert free0 - free1 < 64 << 20  # device-level: far below one N x N bf16 buffer (8 GiB)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+def test_stage_calls_reproduce_fa_backward(dtype, d):
+    """fa_backward_dq then fa_backward_dkdv == fa_backward, bit for bit; the
+    standalone D preprocess agrees with the D that the dQ stage leaves."""
+    B, H, N, scale = 2, 3, 301, 0.11
+    q, k, v, do = (t.to(dev()) for t in make_inputs((B, H, N, d), dtype, 31))
+    o, lse = fa.forward(q, k, v, scale, True)
+    dq1, dk1, dv1 = fa.backward(q, k, v, o, do, lse, scale, True)
+    dt = _lib.FA_BF16 if dtype == torch.bfloat16 else _lib.FA_F32
+    wsb = fa.workspace_bytes(B, H, N, d, dtype)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev())
+    dq2, dk2, dv2 = (torch.full_like(q, float("nan")) for _ in range(3))
+    sp = torch.cuda.current_stream().cuda_stream
+    rc = _lib.fa_backward_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                             lse.data_ptr(), ws.data_ptr(), wsb, dq2.data_ptr(), B, H, N, d, scale,
+                             1, dt, sp)
+    assert rc == _lib.FA_OK
+    d_from_dq = ws[: 4 * B * H * N].view(torch.float32).clone()
+    rc = _lib.fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                               lse.data_ptr(), ws.data_ptr(), wsb, dk2.data_ptr(), dv2.data_ptr(),
+                               B, H, N, d, scale, 1, dt, sp)
+    assert rc == _lib.FA_OK
+    for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2)):
+        assert torch.equal(a, b)
+    rc = _lib.fa_backward_preprocess(o.data_ptr(), do.data_ptr(), ws.data_ptr(), wsb, B, H, N, d,
+                                     dt, sp)
+    assert rc == _lib.FA_OK
+    d_pre = ws[: 4 * B * H * N].view(torch.float32)
+    ref = (o.double() * do.double()).sum(-1).flatten()
+    torch.cuda.synchronize()
+    assert max_abs(d_pre.cpu(), ref.cpu()) < 1e-4
+    assert max_abs(d_from_dq.cpu(), ref.cpu()) < 1e-4
