@@ -45,31 +45,47 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: defer rescaling up to a factor 256
 
-template <int D, int NW, int BC, int ST>
+template <int D, int NW, int RB, int BC, int ST>
 struct FwdCfg {
   static constexpr int NT = NW * kWave;        // threads per workgroup
-  static constexpr int BR = NW * 32;           // query rows per workgroup
+  static constexpr int RW = 32 * RB;           // query rows per wavefront
+  static constexpr int BR = NW * RW;           // query rows per workgroup
   static constexpr int TILE = BC * D;          // elements of one K or V tile
-  static constexpr int LDS_ELEMS = 2 * ST * TILE;  // ST stages of (K, V)
   static constexpr int KSTEPS = D / 16;        // k-steps of K Q^T
   static constexpr int DB = D / 32;            // 32-wide blocks of the head dim
   static constexpr int KB = BC / 32;           // 32-key blocks per tile
   static constexpr int PU = BC / 16;           // k-steps of V^T P^T
   static constexpr int DMA_PER_TILE = TILE / 8 / NT;  // loads per tile per lane
+  static_assert(ST >= 2 && ST <= 3, "two or three K/V stages");
 };
 
 // Per block t: S^T = K Q^T, mask, online softmax, O^T += V^T P^T, with the
 // K/V blocks of the next ST-1 steps in flight (direct buffer->LDS loads).
-template <int D, int NW, int BC, int ST, int OCC, bool CAUSAL>
+// A wavefront owns RB blocks of 32 query rows: every K and V fragment read
+// from LDS feeds RB matrix instructions, which divides LDS reads and
+// HBM->LDS copies per FLOP by RB.
+template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, OCC)
 void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      const bf16_t* __restrict__ V, bf16_t* __restrict__ O,
                      float* __restrict__ LSE, int BH, int N, int nqb, int G, float c) {
-  using C = FwdCfg<D, NW, BC, ST>;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_ELEMS];
-  auto kst = [&](int i) { return lds + (2 * i) * C::TILE; };
-  auto vst = [&](int i) { return lds + (2 * i + 1) * C::TILE; };
-
+  using C = FwdCfg<D, NW, RB, BC, ST>;
+  // One LDS variable per stage and operand: with the stage a compile-time
+  // constant at every access, the compiler can tell the block being read
+  // from the blocks still being copied in, and inserts no wait for them.
+  __shared__ __attribute__((aligned(16))) bf16_t k0s[C::TILE], v0s[C::TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t k1s[ST > 1 ? C::TILE : 8], v1s[ST > 1 ? C::TILE : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t k2s[ST > 2 ? C::TILE : 8], v2s[ST > 2 ? C::TILE : 8];
+  auto kst = [&](auto S) -> bf16_t* {
+    if constexpr (decltype(S)::value == 0) return k0s;
+    else if constexpr (decltype(S)::value == 1) return k1s;
+    else return k2s;
+  };
+  auto vst = [&](auto S) -> bf16_t* {
+    if constexpr (decltype(S)::value == 0) return v0s;
+    else if constexpr (decltype(S)::value == 1) return v1s;
+    else return v2s;
+  };
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
   int bh, rank;
@@ -82,53 +98,69 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   const auto rv = make_rsrc(V + hoff, head_bytes);
 
   const int q0 = qb * C::BR;
-  const int q0w = q0 + w * 32;
-  const int query = q0w + c32;
+  const int q0w = q0 + w * C::RW;  // first query row of this wavefront
+  // this lane's query row in row block rb is q0w + 32 * rb + c32
 
-  // Query fragments: B operand of S^T = K Q^T (lane = query row).
-  bf16x8 qf[C::KSTEPS];
+  // Query fragments: B operands of S^T = K Q^T (lane = query row).
+  bf16x8 qf[RB][C::KSTEPS];
 #pragma unroll
-  for (int s = 0; s < C::KSTEPS; ++s)
-    qf[s] = as_bf16x8(buf_load16(rq, ((uint32_t)query * D + 16 * s + 8 * h) * 2u));
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s)
+      qf[rb][s] = as_bf16x8(
+          buf_load16(rq, ((uint32_t)(q0w + 32 * rb + c32) * D + 16 * s + 8 * h) * 2u));
 
   const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
-  auto fetch = [&](int t) {
-    dma_tile<D, BC, C::NT>(rk, t * BC, kst(t % ST), tid);
-    dma_tile<D, BC, C::NT>(rv, t * BC, vst(t % ST), tid);
+  auto fetch = [&](int t, auto S) {
+    dma_tile<D, BC, C::NT>(rk, t * BC, kst(S), tid);
+    dma_tile<D, BC, C::NT>(rv, t * BC, vst(S), tid);
   };
-  for (int t = 0; t < ST - 1 && t < ntiles; ++t) fetch(t);
+  fetch(0, std::integral_constant<int, 0>{});
+  if constexpr (ST > 2) {
+    if (1 < ntiles) fetch(1, std::integral_constant<int, 1>{});
+  }
   wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - 1));
   __syncthreads();
 
-  f32x16 oacc[C::DB];
+  f32x16 oacc[RB][C::DB];
+  float m[RB], l[RB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+  }
 
-  for (int t = 0; t < ntiles; ++t) {
+  auto step = [&](int t, auto S) {
+    constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
     // the stage of step t-1 is free (barrier at the end of the last step)
-    if (t + ST - 1 < ntiles) fetch(t + ST - 1);
+    if (t + ST - 1 < ntiles) fetch(t + ST - 1, std::integral_constant<int, SN>{});
     const int j0 = t * BC;
-    const bool active = !CAUSAL || j0 <= q0w + 31;
+    const bool active = !CAUSAL || j0 <= q0w + C::RW - 1;
     if (active) {
-      const bf16_t* Ks = kst(t % ST);
-      const bf16_t* Vs = vst(t % ST);
+      const bf16_t* Ks = kst(S);
+      const bf16_t* Vs = vst(S);
 
-      // S^T = K Q^T (lane: query; registers: keys).
-      f32x16 sacc[C::KB];
+      // S^T = K Q^T (lane: query; registers: keys); each K fragment feeds
+      // the RB row blocks.
+      f32x16 sacc[RB][C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         bf16x8 kfr[C::KSTEPS];
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) kfr[s] = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
         const f32x16 z = {};
-        sacc[kb] = mfma32x32x16(kfr[0], qf[0], z);
 #pragma unroll
-        for (int s = 1; s < C::KSTEPS; ++s) sacc[kb] = mfma32x32x16(kfr[s], qf[s], sacc[kb]);
+        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[0], qf[rb][0], z);
+#pragma unroll
+        for (int s = 1; s < C::KSTEPS; ++s)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[s], qf[rb][s], sacc[rb][kb]);
       }
 
       // Causal diagonal and key tail: masked scores become -inf, on the
@@ -136,116 +168,142 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
       const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
       if (need_mask) {
         keep_branch();
-        const int kq = j0 + 4 * h - query;
         const int nk = N - j0 - 4 * h;  // key >= N  <=>  key offset >= nk
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int kq = j0 + 4 * h - (q0w + 32 * rb + c32);
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
+              if ((CAUSAL && kq + koff > 0) || koff >= nk) sacc[rb][kb][r] = -INFINITY;
+            }
+        }
+      }
+
+      // Row maxima; rows whose maximum moved past the slack are rescaled.
+      float muse[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
-            if ((CAUSAL && kq + koff > 0) || koff >= nk) sacc[kb][r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][kb][r]);
+        mx = max_halves(mx) * c;
+        const bool need = mx > m[rb] + kRescaleSlack;
+        if (wave_any(need)) {
+          keep_branch();
+          const float mnew = need ? mx : m[rb];
+          const float alpha = !need ? 1.f : (m[rb] == -INFINITY) ? 0.f : fast_exp2(m[rb] - mnew);
+          m[rb] = mnew;
+          l[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+        }
+        muse[rb] = (m[rb] == -INFINITY) ? 0.f : m[rb];
       }
-
-      // Row maximum; rows whose maximum moved past the slack are rescaled.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = max_halves(mx) * c;
-      const bool need = mx > m + kRescaleSlack;
-      if (wave_any(need)) {
-        keep_branch();
-        const float mnew = need ? mx : m;
-        const float alpha = !need ? 1.f : (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
-        m = mnew;
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      const float muse = (m == -INFINITY) ? 0.f : m;
 
       // P^T as B operand (k-step u: registers 8*(u&1).. of key block u>>1,
-      // i.e. keys 16u + 8*(e>>2) + 4h + (e&3)), then O^T += V^T P^T.
-      float rs[2] = {0.f, 0.f};
+      // i.e. keys 16u + 8*(e>>2) + 4h + (e&3)), then O^T += V^T P^T with
+      // each V fragment feeding the RB row blocks.
 #pragma unroll
       for (int u = 0; u < C::PU; ++u) {
-        uint32_t pw[4];
+        bf16x8 pf[RB];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = fast_exp2(fmaf(sacc[u >> 1][8 * (u & 1) + e], c, -muse));
-          const float p1 = fast_exp2(fmaf(sacc[u >> 1][8 * (u & 1) + e + 1], c, -muse));
-          pw[e >> 1] = pack_bf16x2(p0, p1);
-          rs[(e >> 1) & 1] += p0 + p1;
+        for (int rb = 0; rb < RB; ++rb) {
+          uint32_t pw[4];
+          float rs = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = fast_exp2(fmaf(sacc[rb][u >> 1][8 * (u & 1) + e], c, -muse[rb]));
+            const float p1 = fast_exp2(fmaf(sacc[rb][u >> 1][8 * (u & 1) + e + 1], c, -muse[rb]));
+            pw[e >> 1] = pack_bf16x2(p0, p1);
+            rs += p0 + p1;
+          }
+          l[rb] += rs;
+          pf[rb] = bf16x8_from(pw[0], pw[1], pw[2], pw[3]);
         }
-        const bf16x8 pf = bf16x8_from(pw[0], pw[1], pw[2], pw[3]);
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-          oacc[db] = mfma32x32x16(frag_tr<D>(Vs, 16 * u, db * 32, lane), pf, oacc[db]);
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x8 vfr = frag_tr<D>(Vs, 16 * u, db * 32, lane);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32x32x16(vfr, pf[rb], oacc[rb][db]);
+        }
       }
-      l += rs[0] + rs[1];
     }
     // step t+1 must be resident; later steps may still be in flight
     if (t + 1 < ntiles) {
       wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - t - 2));
       __syncthreads();
     }
+  };
+  for (int t0 = 0; t0 < ntiles; t0 += ST) {
+    step(t0, std::integral_constant<int, 0>{});
+    if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (ST > 2) {
+      if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   // Epilogue: O = acc / l (bf16), LSE = m ln2 + ln l (fp32, natural log).
-  const float lt = sum_halves(l);
-  const float inv = 1.f / lt;
-  if (query < N) {
-    bf16_t* Or = O + hoff + (size_t)query * D;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const int query = q0w + 32 * rb + c32;
+    const float lt = sum_halves(l[rb]);
+    const float inv = 1.f / lt;
+    if (query < N) {
+      bf16_t* Or = O + hoff + (size_t)query * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t lo = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-        const uint32_t hi = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(Or + db * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
-      }
-    if (h == 0) LSE[(size_t)bh * N + query] = fmaf(m, kLn2, logf(lt));
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t lo = pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv);
+          const uint32_t hi = pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(Or + db * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
+        }
+      if (h == 0) LSE[(size_t)bh * N + query] = fmaf(m[rb], kLn2, logf(lt));
+    }
   }
 }
 
-template <int D, int NW, int BC, int ST, int OCC, bool CAUSAL>
+template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL>
 hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                    const Problem& p, hipStream_t stream) {
-  using C = FwdCfg<D, NW, BC, ST>;
+  using C = FwdCfg<D, NW, RB, BC, ST>;
   const int BH = p.B * p.H;
   const int nqb = (p.N + C::BR - 1) / C::BR;
   const long long grid = (long long)BH * nqb;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = p.scale * kLog2e;
   const int G = head_group(OCC * 4 / NW, nqb);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid), dim3(C::NT),
-                     0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O,
-                     LSE, BH, p.N, nqb, G, c);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid),
+                     dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                     (bf16_t*)O, LSE, BH, p.N, nqb, G, c);
   return hipGetLastError();
 }
 
-template <int D, int NW, int BC, int ST, int OCC>
+template <int D, int NW, int RB, int BC, int ST, int OCC>
 hipError_t run_fwd_c(const void* Q, const void* K, const void* V, void* O, float* LSE,
                      const Problem& p, hipStream_t stream) {
-  return p.causal ? run_fwd<D, NW, BC, ST, OCC, true>(Q, K, V, O, LSE, p, stream)
-                  : run_fwd<D, NW, BC, ST, OCC, false>(Q, K, V, O, LSE, p, stream);
+  return p.causal ? run_fwd<D, NW, RB, BC, ST, OCC, true>(Q, K, V, O, LSE, p, stream)
+                  : run_fwd<D, NW, RB, BC, ST, OCC, false>(Q, K, V, O, LSE, p, stream);
 }
 
-// Launch configurations per head dim: wavefronts per workgroup (32 query
-// rows each), keys per K/V block, pipeline stages, minimum wavefronts per
-// SIMD.
+// Launch configurations per head dim: wavefronts per workgroup, 32-row
+// query blocks per wavefront, keys per K/V block, pipeline stages, minimum
+// wavefronts per SIMD.
 #ifndef FA_FWD_CFG_D64
-#define FA_FWD_CFG_D64 4, 32, 2, 4
+#define FA_FWD_CFG_D64 4, 1, 32, 2, 4
 #endif
 #ifndef FA_FWD_CFG_D128
-#define FA_FWD_CFG_D128 4, 64, 2, 2
+#define FA_FWD_CFG_D128 4, 1, 64, 2, 2
 #endif
 #ifndef FA_FWD_CFG_D256
-#define FA_FWD_CFG_D256 4, 32, 2, 1
+#define FA_FWD_CFG_D256 4, 1, 32, 2, 1
 #endif
 
 }  // namespace
