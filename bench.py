@@ -208,8 +208,8 @@ def main(argv=None):
         call(_lib.fa_backward_dq(P[0], P[1], P[2], P[3], P[5], P[4], P[9], wsb, P[6], B, H, N,
                                  d, w.scale, int(w.causal), dt, sp), "fa_backward_dq")
         rec(2)
-        call(_lib.fa_backward_dkdv(P[0], P[1], P[2], P[5], P[4], P[9], wsb, P[7], P[8], B, H, N,
-                                   d, w.scale, int(w.causal), dt, sp), "fa_backward_dkdv")
+        call(_lib.fa_backward_dkdv(P[0], P[1], P[2], P[5], P[9], wsb, P[7], P[8], B, H, N, d,
+                                   w.scale, int(w.causal), dt, sp), "fa_backward_dkdv")
         rec(3)
 
     for _ in range(args.warmup):

@@ -35,8 +35,8 @@ SIGNATURES = {
     "fa_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_backward": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                          _I, _I, _I, _I, _F, _I, _I, _VP]),
-    "fa_backward_preprocess": (_I, [_VP, _VP, _VP, _SZ, _I, _I, _I, _I, _I, _VP]),
-    "fa_backward_dkdv": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP,
+    "fa_backward_preprocess": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _I, _I, _I, _VP]),
+    "fa_backward_dkdv": (_I, [_VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP,
                               _I, _I, _I, _I, _F, _I, _I, _VP]),
     "fa_backward_dq": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP,
                             _I, _I, _I, _I, _F, _I, _I, _VP]),
@@ -99,14 +99,15 @@ def fa_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, 
                                   int(dtype), stream))
 
 
-def fa_backward_preprocess(O, dO, workspace, workspace_bytes, B, H, N, d, dtype, stream) -> int:
-    return int(load().fa_backward_preprocess(O, dO, workspace, workspace_bytes, B, H, N, d,
+def fa_backward_preprocess(O, dO, LSE, workspace, workspace_bytes, B, H, N, d, dtype,
+                           stream) -> int:
+    return int(load().fa_backward_preprocess(O, dO, LSE, workspace, workspace_bytes, B, H, N, d,
                                              int(dtype), stream))
 
 
-def fa_backward_dkdv(Q, K, V, dO, LSE, workspace, workspace_bytes, dK, dV, B, H, N, d, scale,
+def fa_backward_dkdv(Q, K, V, dO, workspace, workspace_bytes, dK, dV, B, H, N, d, scale,
                      causal, dtype, stream) -> int:
-    return int(load().fa_backward_dkdv(Q, K, V, dO, LSE, workspace, workspace_bytes, dK, dV,
+    return int(load().fa_backward_dkdv(Q, K, V, dO, workspace, workspace_bytes, dK, dV,
                                        B, H, N, d, float(scale), int(causal), int(dtype), stream))
 
 

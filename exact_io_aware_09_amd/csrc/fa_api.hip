@@ -70,8 +70,9 @@ int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype) {
   if (check_sizes(B, H, N, d, dtype) != FA_OK) return 0;
-  const size_t bytes = (size_t)B * H * N * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  // D, then LSE * log2(e) from a 256-byte aligned offset
+  const long long rows = (long long)B * H * N;
+  return (size_t)(fa::ws_lse_offset(rows) + fa::ws_lse_offset(rows)) * sizeof(float);
 }
 
 int fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -99,48 +100,49 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_backward_preprocess(const void* O, const void* dO, void* workspace, size_t workspace_bytes,
-                           int B, int H, int N, int d, int dtype, void* stream) {
+int fa_backward_preprocess(const void* O, const void* dO, const float* LSE, void* workspace,
+                           size_t workspace_bytes, int B, int H, int N, int d, int dtype,
+                           void* stream) {
   int rc = check_sizes(B, H, N, d, dtype);
   if (rc != FA_OK) return rc;
-  if (!O || !dO) return FA_ERR_INVALID_ARG;
+  if (!O || !dO || !LSE) return FA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d, dtype))
     return FA_ERR_NO_WORKSPACE;
-  if (!aligned16(O) || !aligned16(dO) || !aligned16(workspace)) return FA_ERR_MISALIGNED;
+  if (!aligned16(O) || !aligned16(dO) || !aligned16(LSE) || !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
   const fa::Problem p{B, H, N, d, 1.0f, false};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* Dws = static_cast<float*>(workspace);
   hipError_t e = (dtype == FA_BF16)
-                     ? fa::launch_backward_bf16(nullptr, nullptr, nullptr, O, dO, nullptr, nullptr,
+                     ? fa::launch_backward_bf16(nullptr, nullptr, nullptr, O, dO, LSE, nullptr,
                                                 nullptr, nullptr, Dws, p, fa::kStagePre, s)
                      : fa::launch_backward_f32(nullptr, nullptr, nullptr, (const float*)O,
-                                               (const float*)dO, nullptr, nullptr, nullptr,
+                                               (const float*)dO, LSE, nullptr, nullptr,
                                                nullptr, Dws, p, fa::kStagePre, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO,
-                     const float* LSE, const void* workspace, size_t workspace_bytes, void* dK,
-                     void* dV, int B, int H, int N, int d, float scale, int causal, int dtype,
-                     void* stream) {
+                     const void* workspace, size_t workspace_bytes, void* dK, void* dV, int B,
+                     int H, int N, int d, float scale, int causal, int dtype, void* stream) {
   int rc = check_common(B, H, N, d, scale, causal, dtype);
   if (rc != FA_OK) return rc;
-  if (!Q || !K || !V || !dO || !LSE || !dK || !dV) return FA_ERR_INVALID_ARG;
+  if (!Q || !K || !V || !dO || !dK || !dV) return FA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d, dtype))
     return FA_ERR_NO_WORKSPACE;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(LSE) ||
-      !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dK) ||
+      !aligned16(dV) || !aligned16(workspace))
     return FA_ERR_MISALIGNED;
   const fa::Problem p{B, H, N, d, scale, causal != 0};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* Dws = const_cast<float*>(static_cast<const float*>(workspace));
   hipError_t e =
       (dtype == FA_BF16)
-          ? fa::launch_backward_bf16(Q, K, V, nullptr, dO, LSE, nullptr, dK, dV, Dws, p,
+          ? fa::launch_backward_bf16(Q, K, V, nullptr, dO, nullptr, nullptr, dK, dV, Dws, p,
                                      fa::kStageDkDv, s)
           : fa::launch_backward_f32((const float*)Q, (const float*)K, (const float*)V, nullptr,
-                                    (const float*)dO, LSE, nullptr, (float*)dK, (float*)dV, Dws, p,
-                                    fa::kStageDkDv, s);
+                                    (const float*)dO, nullptr, nullptr, (float*)dK, (float*)dV,
+                                    Dws, p, fa::kStageDkDv, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

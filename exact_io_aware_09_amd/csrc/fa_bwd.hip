@@ -25,6 +25,8 @@
 // reused stays in registers, softmax statistics are per-lane where possible,
 // and the P / dS fragments produced by one v_mfma_f32_32x32x16_bf16 are fed
 // straight back as the B operand of the next one.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -32,11 +34,13 @@ namespace fa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// D_i = sum_k dO_ik O_ik  (fp32), one row per D/8 lanes (16-byte loads).
+// D_i = sum_k dO_ik O_ik  (fp32), one row per D/8 lanes (16-byte loads),
+// and LSE_i * log2(e) beside it.
 template <int D>
 __global__ __launch_bounds__(256)
 void bwd_pre_bf16_kernel(const bf16_t* __restrict__ O, const bf16_t* __restrict__ dO,
-                         float* __restrict__ Dws, long long rows) {
+                         const float* __restrict__ LSE, float* __restrict__ Dws,
+                         float* __restrict__ Lws, long long rows) {
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
   const int tid = threadIdx.x;
@@ -57,41 +61,80 @@ void bwd_pre_bf16_kernel(const bf16_t* __restrict__ O, const bf16_t* __restrict_
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) Dws[row] = acc;
+  if (row < rows && part == 0) {
+    Dws[row] = acc;
+    Lws[row] = LSE[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV.  Per wavefront: 32 keys whose K and V fragments stay in VGPRs.  Per
-// iteration: a chunk of BQ = 32*QB query rows of Q and dO staged in LDS
-// (swizzled, double-buffered), plus that chunk's LSE*log2(e) and D.  Q and
-// dO are read by rows for S = Q K^T and dP = dO V^T, and through the LDS
-// transpose unit for dK^T += Q^T dS and dV^T += dO^T P.
-template <int D, int NW, int QB>
+// step: a chunk of BQ = 32*QB query rows of Q and dO, with that chunk's
+// LSE*log2(e) and D, copied HBM -> LDS by direct buffer->LDS loads into an
+// ST-stage ring (one LDS variable per stage and operand).  Q and dO are read
+// by rows for S = Q K^T and dP = dO V^T, and through the LDS transpose unit
+// for dK^T += Q^T dS and dV^T += dO^T P.
+template <int D, int NW, int QB, int ST>
 struct DkdvCfg {
   static constexpr int NT = NW * kWave;
   static constexpr int BK = NW * 32;          // keys per workgroup
   static constexpr int BQ = 32 * QB;          // query rows per chunk
   static constexpr int TILE = BQ * D;
-  // one buffer: Q tile, dO tile, then LSE*log2e and D (2*BQ floats)
-  static constexpr int BUF_ELEMS = 2 * TILE + 4 * BQ;
-  static constexpr int CPR = D / 8;
-  static constexpr int CPT = BQ * CPR / NT;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int PU = BQ / 16;
-  static_assert(BQ * CPR % NT == 0, "chunk must split evenly over threads");
-  static_assert(BQ <= NT, "one thread per query row loads LSE and D");
+  // per stage and wavefront: Q and dO tiles, then one 4-byte copy each of
+  // the chunk's LSE*log2e and D
+  static constexpr int DMA_PER_TILE = 2 * (TILE / 8 / NT) + 2;
+  static_assert(BQ <= kWave, "one lane per chunk row copies LSE and D");
+  static_assert(ST >= 2 && ST <= 3, "two or three Q/dO stages");
 };
 
-template <int D, int NW, int QB, int OCC, bool CAUSAL>
+// Copies `rows` consecutive floats starting at row r0 of a per-head float
+// vector into LDS (lane L -> dst[L], rows past the vector's end read as 0).
+// Every wavefront issues the same copy: the writes are identical, so any
+// wavefront's own wait makes the data visible to it.
+template <int ROWS>
+__device__ __forceinline__ void dma_rows_f32(__amdgpu_buffer_rsrc_t r, int r0, float* dst, int lane) {
+  typedef __attribute__((address_space(3))) void* lds_void_ptr;
+  const uint32_t goff = (uint32_t)(r0 + (lane % ROWS)) * 4u;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)dst, 4, goff, 0, 0, 0);
+}
+
+template <int D, int NW, int QB, int ST, int OCC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                           const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
-                          const float* __restrict__ LSE, const float* __restrict__ Dws,
+                          const float* __restrict__ Lws, const float* __restrict__ Dws,
                           bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int BH, int N,
                           int nkb, int G, float c, float scale) {
-  using C = DkdvCfg<D, NW, QB>;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * C::BUF_ELEMS];
+  using C = DkdvCfg<D, NW, QB, ST>;
+  // per stage: Q tile, dO tile, and 64 floats each of LSE*log2e and D
+  __shared__ __attribute__((aligned(16))) bf16_t q0s[C::TILE], o0s[C::TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t q1s[C::TILE], o1s[C::TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t q2s[ST > 2 ? C::TILE : 8], o2s[ST > 2 ? C::TILE : 8];
+  __shared__ __attribute__((aligned(16))) float l0s[kWave], d0s[kWave], l1s[kWave], d1s[kWave];
+  __shared__ __attribute__((aligned(16))) float l2s[ST > 2 ? kWave : 4], d2s[ST > 2 ? kWave : 4];
+  auto qst = [&](auto S) -> bf16_t* {
+    if constexpr (decltype(S)::value == 0) return q0s;
+    else if constexpr (decltype(S)::value == 1) return q1s;
+    else return q2s;
+  };
+  auto ost = [&](auto S) -> bf16_t* {
+    if constexpr (decltype(S)::value == 0) return o0s;
+    else if constexpr (decltype(S)::value == 1) return o1s;
+    else return o2s;
+  };
+  auto lst = [&](auto S) -> float* {
+    if constexpr (decltype(S)::value == 0) return l0s;
+    else if constexpr (decltype(S)::value == 1) return l1s;
+    else return l2s;
+  };
+  auto dst_ = [&](auto S) -> float* {
+    if constexpr (decltype(S)::value == 0) return d0s;
+    else if constexpr (decltype(S)::value == 1) return d1s;
+    else return d2s;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
@@ -101,7 +144,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rq = make_rsrc(Q + hoff, head_bytes);
   const auto ro = make_rsrc(dO + hoff, head_bytes);
-  const auto rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
+  const auto rl = make_rsrc(Lws + (size_t)bh * N, (uint32_t)N * 4u);
   const auto rd = make_rsrc(Dws + (size_t)bh * N, (uint32_t)N * 4u);
 
   const int k0 = kb * C::BK;
@@ -133,54 +176,32 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   const int qstart = CAUSAL ? (k0 / C::BQ) * C::BQ : 0;
   const int nchunks = (N - qstart + C::BQ - 1) / C::BQ;
 
-  uint4 qreg[C::CPT], oreg[C::CPT];
-  float lreg = 0.f, dreg = 0.f;
-  auto gload = [&](int t) {
+  auto fetch = [&](int t, auto S) {
     const int i0 = qstart + t * C::BQ;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int chunk = tid + i * C::NT;
-      const uint32_t off = ((uint32_t)(i0 + chunk / C::CPR) * D + (chunk % C::CPR) * 8) * 2u;
-      qreg[i] = buf_load16(rq, off);
-      oreg[i] = buf_load16(ro, off);
-    }
-    if (tid < C::BQ) {
-      lreg = buf_load_f32(rl, (uint32_t)(i0 + tid) * 4u) * kLog2e;
-      dreg = buf_load_f32(rd, (uint32_t)(i0 + tid) * 4u);
-    }
+    dma_tile<D, C::BQ, C::NT>(rq, i0, qst(S), tid);
+    dma_tile<D, C::BQ, C::NT>(ro, i0, ost(S), tid);
+    dma_rows_f32<C::BQ>(rl, i0, lst(S), lane);
+    dma_rows_f32<C::BQ>(rd, i0, dst_(S), lane);
   };
-  auto lstore = [&](int buf) {
-    bf16_t* Qs = lds + buf * C::BUF_ELEMS;
-    bf16_t* Os = Qs + C::TILE;
-    float* fl = reinterpret_cast<float*>(Qs + 2 * C::TILE);
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int chunk = tid + i * C::NT;
-      const int off = tile_off<D>(chunk / C::CPR, (chunk % C::CPR) * 8);
-      *reinterpret_cast<uint4*>(Qs + off) = qreg[i];
-      *reinterpret_cast<uint4*>(Os + off) = oreg[i];
-    }
-    if (tid < C::BQ) {
-      fl[tid] = lreg;
-      fl[C::BQ + tid] = dreg;
-    }
-  };
-
-  gload(0);
-  lstore(0);
-  wait_vmem_all();
+  wait_vmem_all();  // K and V fragments are in registers before the copies start
+  fetch(0, std::integral_constant<int, 0>{});
+  if constexpr (ST > 2) {
+    if (1 < nchunks) fetch(1, std::integral_constant<int, 1>{});
+  }
+  wait_vmem_tiles<C::DMA_PER_TILE, ST - 2>(min(ST - 2, nchunks - 1));
   __syncthreads();
 
-  for (int t = 0; t < nchunks; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nchunks) gload(t + 1);
+  auto step = [&](int t, auto S) {
+    constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
+    if (t + ST - 1 < nchunks) fetch(t + ST - 1, std::integral_constant<int, SN>{});
     const int i0 = qstart + t * C::BQ;
     // some query of the chunk sees some key of this wavefront
     const bool active = !CAUSAL || i0 + C::BQ - 1 >= k0w;
     if (active) {
-      const bf16_t* Qs = lds + buf * C::BUF_ELEMS;
-      const bf16_t* Os = Qs + C::TILE;
-      const float* fl = reinterpret_cast<const float*>(Qs + 2 * C::TILE);
+      const bf16_t* Qs = qst(S);
+      const bf16_t* Os = ost(S);
+      const float* ls = lst(S);
+      const float* ds = dst_(S);
 
       // S = Q K^T and dP = dO V^T (lane: key; registers: query rows).
       f32x16 sacc[QB], pacc[QB];
@@ -201,17 +222,17 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
         }
       }
 
-      // P = exp2(S c - LSE2); masked entries (causal future, query tail) are
-      // zeroed on the blocks that need it only (a real branch).
-      float pv[QB][16];
+      // P = exp2(S c - LSE2), in place; masked entries (causal future, query
+      // tail) are zeroed on the blocks that need it only (a real branch).
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           // rows 8g + 4h + 0..3 of this 32-row block: one 16-byte LDS read
-          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(fl + qb * 32 + 8 * g + 4 * h);
+          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * g + 4 * h);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pv[qb][4 * g + e] = fast_exp2(fmaf(sacc[qb][4 * g + e], c, -lse4[e]));
+          for (int e = 0; e < 4; ++e)
+            sacc[qb][4 * g + e] = fast_exp2(fmaf(sacc[qb][4 * g + e], c, -lse4[e]));
         }
       const bool need_mask = (i0 + C::BQ > N) || (CAUSAL && i0 < k0w + 31);
       if (need_mask) {
@@ -223,7 +244,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
-            if ((CAUSAL && kqh > qoff) || qoff >= nq) pv[qb][r] = 0.f;
+            if ((CAUSAL && kqh > qoff) || qoff >= nq) sacc[qb][r] = 0.f;
           }
       }
       // dS = P (dP - D); P and dS packed to bf16 as B operands (k-step
@@ -233,15 +254,15 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 dd4 = *reinterpret_cast<const f32x4*>(fl + C::BQ + qb * 32 + 8 * g + 4 * h);
-          float ds[4];
+          const f32x4 dd4 = *reinterpret_cast<const f32x4*>(ds + qb * 32 + 8 * g + 4 * h);
+          float dsv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ds[e] = pv[qb][4 * g + e] * (pacc[qb][4 * g + e] - dd4[e]);
+          for (int e = 0; e < 4; ++e) dsv[e] = sacc[qb][4 * g + e] * (pacc[qb][4 * g + e] - dd4[e]);
           const int u = 2 * qb + (g >> 1), w0 = 2 * (g & 1);
-          pw[u][w0] = pack_bf16x2(pv[qb][4 * g], pv[qb][4 * g + 1]);
-          pw[u][w0 + 1] = pack_bf16x2(pv[qb][4 * g + 2], pv[qb][4 * g + 3]);
-          sw[u][w0] = pack_bf16x2(ds[0], ds[1]);
-          sw[u][w0 + 1] = pack_bf16x2(ds[2], ds[3]);
+          pw[u][w0] = pack_bf16x2(sacc[qb][4 * g], sacc[qb][4 * g + 1]);
+          pw[u][w0 + 1] = pack_bf16x2(sacc[qb][4 * g + 2], sacc[qb][4 * g + 3]);
+          sw[u][w0] = pack_bf16x2(dsv[0], dsv[1]);
+          sw[u][w0 + 1] = pack_bf16x2(dsv[2], dsv[3]);
         }
 
       // dV^T += dO^T P,  dK^T += Q^T dS  (lane: key; registers: head dims).
@@ -256,8 +277,18 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
         }
       }
     }
-    if (t + 1 < nchunks) lstore(buf ^ 1);
-    __syncthreads();
+    // step t+1 must be resident; later steps may still be in flight
+    if (t + 1 < nchunks) {
+      wait_vmem_tiles<C::DMA_PER_TILE, ST - 2>(min(ST - 2, nchunks - t - 2));
+      __syncthreads();
+    }
+  };
+  for (int t0 = 0; t0 < nchunks; t0 += ST) {
+    step(t0, std::integral_constant<int, 0>{});
+    if (t0 + 1 < nchunks) step(t0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (ST > 2) {
+      if (t0 + 2 < nchunks) step(t0 + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   if (key < N) {
@@ -281,34 +312,49 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// dQ.  Per wavefront: 32 query rows (Q and dO fragments in VGPRs, LSE and D
-// per lane; D is formed here and stored for the dK/dV kernel).  Per iteration: a block of BC keys of K and V in LDS (swizzled,
-// double-buffered): K and V read by rows for S^T = K Q^T and dP^T = V dO^T,
-// K through the transpose unit for dQ^T += K^T dS^T.
-template <int D, int NW, int BC>
+// dQ.  Per wavefront: RB blocks of 32 query rows (Q and dO fragments in
+// VGPRs, LSE and D per lane; D is formed here and stored for the dK/dV
+// kernel, beside LSE*log2(e)).  Per step: a block of BC keys of K and V, copied HBM -> LDS by
+// direct buffer->LDS loads into an ST-stage ring (one LDS variable per
+// stage, so reads of the current block never wait for the copies in
+// flight): K and V read by rows for S^T = K Q^T and dP^T = V dO^T, K
+// through the transpose unit for dQ^T += K^T dS^T.  Each fragment read
+// from LDS feeds the RB row blocks.
+template <int D, int NW, int RB, int BC, int ST>
 struct DqCfg {
   static constexpr int NT = NW * kWave;
-  static constexpr int BR = NW * 32;
+  static constexpr int RW = 32 * RB;          // query rows per wavefront
+  static constexpr int BR = NW * RW;          // query rows per workgroup
   static constexpr int TILE = BC * D;
-  static constexpr int BUF_ELEMS = 2 * TILE;
-  static constexpr int CPR = D / 8;
-  static constexpr int CPT = BC * CPR / NT;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int KB = BC / 32;
   static constexpr int PU = BC / 16;
-  static_assert(BC * CPR % NT == 0, "tile must split evenly over threads");
+  static constexpr int DMA_PER_TILE = TILE / 8 / NT;
+  static_assert(ST >= 2 && ST <= 3, "two or three K/V stages");
 };
 
-template <int D, int NW, int BC, int OCC, bool CAUSAL>
+template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                         const bf16_t* __restrict__ V, const bf16_t* __restrict__ O,
                         const bf16_t* __restrict__ dO, const float* __restrict__ LSE,
-                        float* __restrict__ Dws, bf16_t* __restrict__ dQ, int BH, int N, int nqb,
-                        int G, float c, float scale) {
-  using C = DqCfg<D, NW, BC>;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * C::BUF_ELEMS];
+                        float* __restrict__ Dws, float* __restrict__ Lws, bf16_t* __restrict__ dQ,
+                        int BH, int N, int nqb, int G, float c, float scale) {
+  using C = DqCfg<D, NW, RB, BC, ST>;
+  __shared__ __attribute__((aligned(16))) bf16_t k0s[C::TILE], v0s[C::TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t k1s[C::TILE], v1s[C::TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t k2s[ST > 2 ? C::TILE : 8], v2s[ST > 2 ? C::TILE : 8];
+  auto kst = [&](auto S) -> bf16_t* {
+    if constexpr (decltype(S)::value == 0) return k0s;
+    else if constexpr (decltype(S)::value == 1) return k1s;
+    else return k2s;
+  };
+  auto vst = [&](auto S) -> bf16_t* {
+    if constexpr (decltype(S)::value == 0) return v0s;
+    else if constexpr (decltype(S)::value == 1) return v1s;
+    else return v2s;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
@@ -321,198 +367,219 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
   const auto rv = make_rsrc(V + hoff, head_bytes);
 
   const int q0 = qb * C::BR;
-  const int q0w = q0 + w * 32;
-  const int query = q0w + c32;
+  const int q0w = q0 + w * C::RW;  // row block rb of this lane: query q0w + 32 rb + c32
 
   // Q and dO fragments (B operands, lane = query row: half h holds head dims
   // 16s + 8h .. +7), LSE in log2 units, and D_i = sum_k dO_ik O_ik formed
   // here from the matching O fragment and stored for the dK/dV kernel.
-  bf16x8 qf[C::KSTEPS], of[C::KSTEPS];
-  float lse2, dd;
+  bf16x8 qf[RB][C::KSTEPS], of[RB][C::KSTEPS];
+  float lse2[RB], dd[RB];
   {
     const auto rq = make_rsrc(Q + hoff, head_bytes);
     const auto ro = make_rsrc(dO + hoff, head_bytes);
     const auto rO = make_rsrc(O + hoff, head_bytes);
-    bf16x8 ov[C::KSTEPS];
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
-      const uint32_t off = ((uint32_t)query * D + 16 * s + 8 * h) * 2u;
-      qf[s] = as_bf16x8(buf_load16(rq, off));
-      of[s] = as_bf16x8(buf_load16(ro, off));
-      ov[s] = as_bf16x8(buf_load16(rO, off));
-    }
     const auto rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
-    lse2 = buf_load_f32(rl, (uint32_t)query * 4u) * kLog2e;
-    float part = 0.f;
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s)
+    for (int rb = 0; rb < RB; ++rb) {
+      const int query = q0w + 32 * rb + c32;
+      bf16x8 ov[C::KSTEPS];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part = fmaf((float)of[s][e], (float)ov[s][e], part);
-    dd = sum_halves(part);
-    if (h == 0 && query < N) Dws[(size_t)bh * N + query] = dd;
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        const uint32_t off = ((uint32_t)query * D + 16 * s + 8 * h) * 2u;
+        qf[rb][s] = as_bf16x8(buf_load16(rq, off));
+        of[rb][s] = as_bf16x8(buf_load16(ro, off));
+        ov[s] = as_bf16x8(buf_load16(rO, off));
+      }
+      lse2[rb] = buf_load_f32(rl, (uint32_t)query * 4u) * kLog2e;
+      float part = 0.f;
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf((float)of[rb][s][e], (float)ov[s][e], part);
+      dd[rb] = sum_halves(part);
+      if (h == 0 && query < N) {
+        Dws[(size_t)bh * N + query] = dd[rb];
+        Lws[(size_t)bh * N + query] = lse2[rb];
+      }
+    }
   }
 
-  f32x16 dqacc[C::DB];
+  f32x16 dqacc[RB][C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqacc[rb][db][r] = 0.f;
 
   const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
-  uint4 kreg[C::CPT], vreg[C::CPT];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int chunk = tid + i * C::NT;
-      const uint32_t off = ((uint32_t)(t * BC + chunk / C::CPR) * D + (chunk % C::CPR) * 8) * 2u;
-      kreg[i] = buf_load16(rk, off);
-      vreg[i] = buf_load16(rv, off);
-    }
+  auto fetch = [&](int t, auto S) {
+    dma_tile<D, BC, C::NT>(rk, t * BC, kst(S), tid);
+    dma_tile<D, BC, C::NT>(rv, t * BC, vst(S), tid);
   };
-  auto lstore = [&](int buf) {
-    bf16_t* Ks = lds + buf * C::BUF_ELEMS;
-    bf16_t* Vs = Ks + C::TILE;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int chunk = tid + i * C::NT;
-      const int off = tile_off<D>(chunk / C::CPR, (chunk % C::CPR) * 8);
-      *reinterpret_cast<uint4*>(Ks + off) = kreg[i];
-      *reinterpret_cast<uint4*>(Vs + off) = vreg[i];
-    }
-  };
-
-  gload(0);
-  lstore(0);
-  wait_vmem_all();
+  wait_vmem_all();  // Q, dO, O, LSE are in registers before the copies start
+  fetch(0, std::integral_constant<int, 0>{});
+  if constexpr (ST > 2) {
+    if (1 < ntiles) fetch(1, std::integral_constant<int, 1>{});
+  }
+  wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - 1));
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
+  auto step = [&](int t, auto S) {
+    constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
+    if (t + ST - 1 < ntiles) fetch(t + ST - 1, std::integral_constant<int, SN>{});
     const int j0 = t * BC;
-    const bool active = !CAUSAL || j0 <= q0w + 31;
+    const bool active = !CAUSAL || j0 <= q0w + C::RW - 1;
     if (active) {
-      const bf16_t* Ks = lds + buf * C::BUF_ELEMS;
-      const bf16_t* Vs = Ks + C::TILE;
+      const bf16_t* Ks = kst(S);
+      const bf16_t* Vs = vst(S);
 
       // S^T = K Q^T, dP^T = V dO^T (lane: query; registers: keys).
-      f32x16 sacc[C::KB], pacc[C::KB];
+      f32x16 sacc[RB][C::KB], pacc[RB][C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
           const bf16x8 ak = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
           const bf16x8 av = frag_rows<D>(Vs, kb * 32, 16 * s, c32, h);
-          if (s == 0) {
-            const f32x16 z = {};
-            sacc[kb] = mfma32x32x16(ak, qf[s], z);
-            pacc[kb] = mfma32x32x16(av, of[s], z);
-          } else {
-            sacc[kb] = mfma32x32x16(ak, qf[s], sacc[kb]);
-            pacc[kb] = mfma32x32x16(av, of[s], pacc[kb]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            if (s == 0) {
+              const f32x16 z = {};
+              sacc[rb][kb] = mfma32x32x16(ak, qf[rb][s], z);
+              pacc[rb][kb] = mfma32x32x16(av, of[rb][s], z);
+            } else {
+              sacc[rb][kb] = mfma32x32x16(ak, qf[rb][s], sacc[rb][kb]);
+              pacc[rb][kb] = mfma32x32x16(av, of[rb][s], pacc[rb][kb]);
+            }
           }
         }
       }
 
-      // P^T = exp2(S^T c - LSE2); masked entries (causal future, key tail) are
-      // zeroed on the blocks that need it only (a real branch).
-      float pv[C::KB][16];
+      // P^T = exp2(S^T c - LSE2), in place; masked entries (causal future,
+      // key tail) are zeroed on the blocks that need it only (a real branch).
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pv[kb][r] = fast_exp2(fmaf(sacc[kb][r], c, -lse2));
-      const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
-      if (need_mask) {
-        keep_branch();
-        const int kq = j0 + 4 * h - query;  // key - query = kq + key offset
-        const int nk = N - j0 - 4 * h;      // key >= N  <=>  key offset >= nk
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
-            if ((CAUSAL && kq + koff > 0) || koff >= nk) pv[kb][r] = 0.f;
-          }
+          for (int r = 0; r < 16; ++r) sacc[rb][kb][r] = fast_exp2(fmaf(sacc[rb][kb][r], c, -lse2[rb]));
+      const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
+      if (need_mask) {
+        keep_branch();
+        const int nk = N - j0 - 4 * h;  // key >= N  <=>  key offset >= nk
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int kq = j0 + 4 * h - (q0w + 32 * rb + c32);  // key - query = kq + key offset
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
+              if ((CAUSAL && kq + koff > 0) || koff >= nk) sacc[rb][kb][r] = 0.f;
+            }
+        }
       }
       // dS^T = P^T (dP^T - D), packed to bf16: register r of block kb is
-      // k-step 2*kb + (r>>3), element r & 7.
-      uint32_t sw[C::PU][4];
+      // k-step 2*kb + (r>>3), element r & 7; then dQ^T += K^T dS^T (lane:
+      // query; registers: head dims), each K^T fragment feeding RB blocks.
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+      for (int u = 0; u < C::PU; ++u) {
+        bf16x8 sf[RB];
 #pragma unroll
-        for (int r = 0; r < 16; r += 2)
-          sw[2 * kb + (r >> 3)][(r & 7) >> 1] =
-              pack_bf16x2(pv[kb][r] * (pacc[kb][r] - dd), pv[kb][r + 1] * (pacc[kb][r + 1] - dd));
-
-      // dQ^T += K^T dS^T (lane: query; registers: head dims).
+        for (int rb = 0; rb < RB; ++rb) {
+          uint32_t sw[4];
+          const int kb = u >> 1, r0 = 8 * (u & 1);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
+          for (int e = 0; e < 8; e += 2)
+            sw[e >> 1] = pack_bf16x2(sacc[rb][kb][r0 + e] * (pacc[rb][kb][r0 + e] - dd[rb]),
+                                     sacc[rb][kb][r0 + e + 1] * (pacc[rb][kb][r0 + e + 1] - dd[rb]));
+          sf[rb] = bf16x8_from(sw[0], sw[1], sw[2], sw[3]);
+        }
 #pragma unroll
-        for (int u = 0; u < C::PU; ++u) {
+        for (int db = 0; db < C::DB; ++db) {
           const bf16x8 a = frag_tr<D>(Ks, 16 * u, db * 32, lane);
-          dqacc[db] = mfma32x32x16(a, bf16x8_from(sw[u][0], sw[u][1], sw[u][2], sw[u][3]), dqacc[db]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) dqacc[rb][db] = mfma32x32x16(a, sf[rb], dqacc[rb][db]);
         }
       }
     }
-    if (t + 1 < ntiles) lstore(buf ^ 1);
-    __syncthreads();
+    // step t+1 must be resident; later steps may still be in flight
+    if (t + 1 < ntiles) {
+      wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - t - 2));
+      __syncthreads();
+    }
+  };
+  for (int t0 = 0; t0 < ntiles; t0 += ST) {
+    step(t0, std::integral_constant<int, 0>{});
+    if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (ST > 2) {
+      if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>{});
+    }
   }
 
-  if (query < N) {
-    bf16_t* dQr = dQ + hoff + (size_t)query * D;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const int query = q0w + 32 * rb + c32;
+    if (query < N) {
+      bf16_t* dQr = dQ + hoff + (size_t)query * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v;
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = to_bf16(dqacc[db][4 * g + e] * scale);
-        *reinterpret_cast<bf16x4*>(dQr + db * 32 + 8 * g + 4 * h) = v;
-      }
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = to_bf16(dqacc[rb][db][4 * g + e] * scale);
+          *reinterpret_cast<bf16x4*>(dQr + db * 32 + 8 * g + 4 * h) = v;
+        }
+    }
   }
 }
 
-template <int D, int NWK, int QB, int OCCK, int NWQ, int BC, int OCCQ, bool CAUSAL>
+template <int D, int NWK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ, int OCCQ,
+          bool CAUSAL>
 hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                   const float* LSE, void* dQ, void* dK, void* dV, float* Dws, const Problem& p,
+                   const float* LSE, void* dQ, void* dK, void* dV, float* ws, const Problem& p,
                    unsigned stages, hipStream_t stream) {
   const int BH = p.B * p.H;
   const long long rows = (long long)BH * p.N;
   const float c = p.scale * kLog2e;
+  float* Dws = ws;         // D, one float per row
+  float* Lws = ws + ws_lse_offset(rows);  // LSE * log2(e), one float per row
   if (stages & kStagePre) {
     constexpr int RPB = 256 / (D / 8);
     const long long grid = (rows + RPB - 1) / RPB;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_pre_bf16_kernel<D>), dim3((unsigned)grid), dim3(256), 0, stream,
-                       (const bf16_t*)O, (const bf16_t*)dO, Dws, rows);
+                       (const bf16_t*)O, (const bf16_t*)dO, LSE, Dws, Lws, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kStageDq) {
-    using C = DqCfg<D, NWQ, BC>;
+    using C = DqCfg<D, NWQ, RBQ, BC, STQ>;
     const int nqb = (p.N + C::BR - 1) / C::BR;
     const long long grid = (long long)BH * nqb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int G = head_group(OCCQ * 4 / NWQ, nqb);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, BC, OCCQ, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
-                       stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                       (const bf16_t*)O, (const bf16_t*)dO, LSE, Dws, (bf16_t*)dQ, BH, p.N, nqb, G,
-                       c, p.scale);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, RBQ, BC, STQ, OCCQ, CAUSAL>), dim3((unsigned)grid),
+                       dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                       (const bf16_t*)O, (const bf16_t*)dO, LSE, Dws, Lws, (bf16_t*)dQ, BH, p.N, nqb,
+                       G, c, p.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kStageDkDv) {
-    using C = DkdvCfg<D, NWK, QB>;
+    using C = DkdvCfg<D, NWK, QB, STK>;
     const int nkb = (p.N + C::BK - 1) / C::BK;
     const long long grid = (long long)BH * nkb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int G = head_group(OCCK * 4 / NWK, nkb);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, QB, OCCK, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
-                       stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                       (const bf16_t*)dO, LSE, Dws, (bf16_t*)dK, (bf16_t*)dV, BH, p.N, nkb, G, c,
-                       p.scale);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, QB, STK, OCCK, CAUSAL>), dim3((unsigned)grid),
+                       dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                       (const bf16_t*)dO, (const float*)Lws, (const float*)Dws, (bf16_t*)dK,
+                       (bf16_t*)dV, BH, p.N, nkb, G, c, p.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -520,26 +587,27 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
 }
 
 // Launch configurations per head dim: dK/dV (wavefronts per workgroup,
-// 32-row query blocks per chunk, minimum wavefronts per SIMD), then dQ
-// (wavefronts per workgroup, keys per K/V block, minimum wavefronts per SIMD).
+// 32-row query blocks per chunk, Q/dO stages, minimum wavefronts per SIMD),
+// then dQ (wavefronts per workgroup, 32-row query blocks per wavefront, keys
+// per K/V block, K/V stages, minimum wavefronts per SIMD).
 #ifndef FA_BWD_CFG_D64
-#define FA_BWD_CFG_D64 4, 2, 2, 4, 64, 2
+#define FA_BWD_CFG_D64 4, 2, 2, 2, 4, 1, 32, 2, 3
 #endif
 #ifndef FA_BWD_CFG_D128
-#define FA_BWD_CFG_D128 4, 1, 1, 4, 64, 1
+#define FA_BWD_CFG_D128 4, 1, 2, 1, 4, 1, 64, 2, 1
 #endif
 #ifndef FA_BWD_CFG_D256
-#define FA_BWD_CFG_D256 4, 1, 1, 4, 32, 1
+#define FA_BWD_CFG_D256 4, 1, 2, 1, 4, 1, 32, 2, 1
 #endif
 
-template <int D, int NWK, int QB, int OCCK, int NWQ, int BC, int OCCQ>
+template <int D, int NWK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ, int OCCQ>
 hipError_t run_bwd_c(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                     const float* LSE, void* dQ, void* dK, void* dV, float* Dws, const Problem& p,
+                     const float* LSE, void* dQ, void* dK, void* dV, float* ws, const Problem& p,
                      unsigned stages, hipStream_t stream) {
-  return p.causal ? run_bwd<D, NWK, QB, OCCK, NWQ, BC, OCCQ, true>(Q, K, V, O, dO, LSE, dQ, dK, dV,
-                                                                  Dws, p, stages, stream)
-                  : run_bwd<D, NWK, QB, OCCK, NWQ, BC, OCCQ, false>(Q, K, V, O, dO, LSE, dQ, dK,
-                                                                   dV, Dws, p, stages, stream);
+  return p.causal ? run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true>(
+                        Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, stream)
+                  : run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false>(
+                        Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, stream);
 }
 
 }  // namespace

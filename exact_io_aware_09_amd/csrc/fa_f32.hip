@@ -116,7 +116,8 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 template <int D>
 __global__ __launch_bounds__(256)
 void bwd_pre_f32_kernel(const float* __restrict__ O, const float* __restrict__ dO,
-                        float* __restrict__ Dws, long long rows) {
+                        const float* __restrict__ LSE, float* __restrict__ Dws,
+                        float* __restrict__ Lws, long long rows) {
   constexpr int TPR = D / 16, RPB = 256 / TPR;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
@@ -128,14 +129,17 @@ void bwd_pre_f32_kernel(const float* __restrict__ O, const float* __restrict__ d
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc = fmaf(a[e], b[e], acc);
   acc = group_sum<TPR>(acc);
-  if (ok && part == 0) Dws[row] = acc;
+  if (ok && part == 0) {
+    Dws[row] = acc;
+    Lws[row] = LSE[row] * kLog2e;
+  }
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256)
 void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                          const float* __restrict__ V, const float* __restrict__ dO,
-                         const float* __restrict__ LSE, const float* __restrict__ Dws,
+                         const float* __restrict__ Lws, const float* __restrict__ Dws,
                          float* __restrict__ dK, float* __restrict__ dV, int N, int nkb,
                          float scale) {
   constexpr int TPR = D / 16, RPB = 256 / TPR;
@@ -159,7 +163,7 @@ void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     stage_rows<D>(Os, dO + hoff, i0, N);
     if (threadIdx.x < kTile) {
       const int r = i0 + threadIdx.x;
-      Ls[threadIdx.x] = r < N ? LSE[(size_t)bh * N + r] : 0.f;
+      Ls[threadIdx.x] = r < N ? Lws[(size_t)bh * N + r] : 0.f;  // LSE * log2(e)
       Ds[threadIdx.x] = r < N ? Dws[(size_t)bh * N + r] : 0.f;
     }
     __syncthreads();
@@ -174,7 +178,7 @@ void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
       dp = group_sum<TPR>(dp);
       const int query = i0 + i;
       const bool vis = query < N && (!CAUSAL || key <= query);
-      const float p = vis ? expf(s - Ls[i]) : 0.f;
+      const float p = vis ? exp2f(fmaf(s, kLog2e, -Ls[i])) : 0.f;
       const float ds = p * (dp - Ds[i]);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -263,18 +267,20 @@ hipError_t run_fwd_f32(const float* Q, const float* K, const float* V, float* O,
 template <int D, bool CAUSAL>
 hipError_t run_bwd_f32(const float* Q, const float* K, const float* V, const float* O,
                        const float* dO, const float* LSE, float* dQ, float* dK, float* dV,
-                       float* Dws, const Problem& p, unsigned stages, hipStream_t stream) {
+                       float* ws, const Problem& p, unsigned stages, hipStream_t stream) {
   constexpr int RPB = 256 / (D / 16);
   const long long rows = (long long)p.B * p.H * p.N;
+  float* Dws = ws;         // D, one float per row
+  float* Lws = ws + ws_lse_offset(rows);  // LSE * log2(e), one float per row
   const long long gpre = (rows + RPB - 1) / RPB;
   const int nb = (p.N + RPB - 1) / RPB;
   const long long grid = (long long)p.B * p.H * nb;
   if (gpre > 0x7fffffffLL || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  // the dQ stage forms D itself (here with the standalone kernel) and leaves
-  // it in the workspace for the dK/dV stage
+  // the dQ stage forms D and LSE*log2(e) itself (here with the standalone
+  // kernel) and leaves them in the workspace for the dK/dV stage
   if (stages & (kStagePre | kStageDq)) {
     hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)gpre), dim3(256), 0, stream, O, dO,
-                       Dws, rows);
+                       LSE, Dws, Lws, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -286,7 +292,8 @@ hipError_t run_bwd_f32(const float* Q, const float* K, const float* V, const flo
   }
   if (stages & kStageDkDv) {
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, Q, K, V, dO, LSE, Dws, dK, dV, p.N, nb, p.scale);
+                       stream, Q, K, V, dO, (const float*)Lws, (const float*)Dws, dK, dV, p.N, nb,
+                       p.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

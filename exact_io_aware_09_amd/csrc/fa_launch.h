@@ -13,10 +13,14 @@ struct Problem {
 // bfloat16 inputs, fp32 accumulation on the matrix cores.
 hipError_t launch_forward_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                const Problem& p, hipStream_t stream);
+// Backward workspace: D (one float per query row), then, starting at float
+// index ws_lse_offset(rows), LSE * log2(e) (one float per row).
+inline long long ws_lse_offset(long long rows) { return (rows + 63) & ~63LL; }
+
 // Backward stages, enqueued in this order when several bits are set:
-//   kStagePre   D = rowsum(dO * O) into the workspace;
-//   kStageDq    dQ; also forms D from O and dO and stores it in the workspace;
-//   kStageDkDv  dK, dV; reads D from the workspace.
+//   kStagePre   D = rowsum(dO * O) and LSE * log2(e) into the workspace;
+//   kStageDq    dQ; also forms both workspace vectors and stores them;
+//   kStageDkDv  dK, dV; reads both vectors from the workspace.
 enum : unsigned { kStagePre = 1u, kStageDq = 2u, kStageDkDv = 4u, kStagesGrad = 6u };
 
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,

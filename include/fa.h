@@ -78,9 +78,10 @@ int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
                void* stream);
 
 /*
- * Bytes of device workspace fa_backward needs: one float32 per query row
- * (the D vector of CS324 notes section 5.4), rounded up to 256 bytes.
- * Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_backward needs: two float32 vectors of one
+ * value per query row (B*H*N rows), each starting on a 256-byte boundary --
+ * D_i = sum_k dO_ik O_ik (the vector of CS324 notes section 5.4) and
+ * LSE_i * log2(e).  Returns 0 for invalid sizes.
  */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype);
 
@@ -88,12 +89,13 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype);
  * Backward pass.  Reads Q, K, V, O, dO and the forward's LSE; writes dQ, dK,
  * dV (all [B,H,N,d], dtype) completely (no accumulation into the caller's
  * buffers).  `workspace` (device memory of at least
- * fa_backward_workspace_bytes(), contents ignored on entry) receives D.
- * Two kernels are enqueued on `stream`, in order: a dQ kernel (one Q block
- * per workgroup, loop over K/V blocks) that also forms D = rowsum(dO * O)
- * for its rows and stores it in `workspace`; then a dK/dV kernel (one K/V
- * block per workgroup, loop over Q blocks) that reads D.  No atomics:
- * results are bitwise reproducible run to run.
+ * fa_backward_workspace_bytes(), contents ignored on entry) receives D and
+ * LSE * log2(e).  Two kernels are enqueued on `stream`, in order: a dQ
+ * kernel (one Q block per workgroup, loop over K/V blocks) that also forms
+ * D = rowsum(dO * O) and LSE * log2(e) for its rows and stores them in
+ * `workspace`; then a dK/dV kernel (one K/V block per workgroup, loop over
+ * Q blocks) that reads them.  No atomics: results are bitwise reproducible
+ * run to run.
  */
 int fa_backward(const void* Q, const void* K, const void* V, const void* O,
                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
@@ -109,27 +111,27 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O,
  *
  * fa_backward_dq:   reads Q, K, V, O, dO and LSE; writes dQ, and writes D
  *   (D_i = sum_k dO_ik O_ik, float32: the identity of CS324 notes section
- *   5.4 that replaces sum_j P_ij dP_ij) into `workspace`.
- * fa_backward_dkdv: reads Q, K, V, dO, LSE and D (workspace); writes dK, dV.
- *   D must come from fa_backward_dq or fa_backward_preprocess on the same
- *   O and dO, enqueued earlier.
- * fa_backward_preprocess: D alone into `workspace` (a streaming pass over O
- *   and dO), for callers that run fa_backward_dkdv without fa_backward_dq.
- *   Its D may differ from fa_backward_dq's in the last bits (different
- *   summation order).
+ *   5.4 that replaces sum_j P_ij dP_ij) and LSE * log2(e) into `workspace`.
+ * fa_backward_dkdv: reads Q, K, V, dO and the two workspace vectors; writes
+ *   dK, dV.  The workspace must have been filled by fa_backward_dq or
+ *   fa_backward_preprocess on the same O, dO and LSE, enqueued earlier.
+ * fa_backward_preprocess: the two workspace vectors alone (a streaming pass
+ *   over O, dO and LSE), for callers that run fa_backward_dkdv without
+ *   fa_backward_dq.  Its D may differ from fa_backward_dq's in the last bits
+ *   (different summation order).
  * Errors and argument rules are those of fa_backward.
  */
-int fa_backward_preprocess(const void* O, const void* dO, void* workspace, size_t workspace_bytes,
-                           int B, int H, int N, int d, int dtype, void* stream);
+int fa_backward_preprocess(const void* O, const void* dO, const float* LSE, void* workspace,
+                           size_t workspace_bytes, int B, int H, int N, int d, int dtype,
+                           void* stream);
 
 int fa_backward_dq(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                    const float* LSE, void* workspace, size_t workspace_bytes, void* dQ, int B,
                    int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 int fa_backward_dkdv(const void* Q, const void* K, const void* V, const void* dO,
-                     const float* LSE, const void* workspace, size_t workspace_bytes,
-                     void* dK, void* dV, int B, int H, int N, int d, float scale, int causal,
-                     int dtype, void* stream);
+                     const void* workspace, size_t workspace_bytes, void* dK, void* dV, int B,
+                     int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

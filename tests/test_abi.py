@@ -71,15 +71,17 @@ def test_forward_validation(args, code):
 
 
 def test_workspace_bytes():
-    assert fa.fa_backward_workspace_bytes(64, 16, 1024, 64, 0) == 64 * 16 * 1024 * 4
-    assert fa.fa_backward_workspace_bytes(1, 1, 1, 64, 0) == 256
+    # two float32 vectors (D and LSE*log2 e), each padded to 256 bytes
+    assert fa.fa_backward_workspace_bytes(64, 16, 1024, 64, 0) == 2 * 64 * 16 * 1024 * 4
+    assert fa.fa_backward_workspace_bytes(1, 1, 1, 64, 0) == 512
+    assert fa.fa_backward_workspace_bytes(1, 3, 100, 64, 1) == 2 * 1280
     assert fa.fa_backward_workspace_bytes(1, 1, 0, 64, 0) == 0
     assert fa.fa_backward_workspace_bytes(1, 1, 8, 96, 0) == 0
 
 
 @pytest.mark.parametrize("args,code", [
     (dict(workspace=0), _lib.FA_ERR_NO_WORKSPACE),
-    (dict(workspace_bytes=255), _lib.FA_ERR_NO_WORKSPACE),
+    (dict(workspace_bytes=511), _lib.FA_ERR_NO_WORKSPACE),
     (dict(dO=0), _lib.FA_ERR_INVALID_ARG),
     (dict(dV=A + 8), _lib.FA_ERR_MISALIGNED),
     (dict(workspace=A + 8), _lib.FA_ERR_MISALIGNED),
@@ -88,7 +90,7 @@ def test_workspace_bytes():
 ])
 def test_backward_validation(args, code):
     kw = dict(Q=A, K=A, V=A, O=A, dO=A, LSE=A, dQ=A, dK=A, dV=A, workspace=A,
-              workspace_bytes=256, B=1, H=1, N=16, d=64, scale=0.125, causal=1,
+              workspace_bytes=512, B=1, H=1, N=16, d=64, scale=0.125, causal=1,
               dtype=_lib.FA_BF16, stream=None)
     kw.update(args)
     assert fa.fa_backward(**kw) == code

@@ -324,18 +324,33 @@ def test_stage_calls_reproduce_fa_backward(dtype, d):
                              lse.data_ptr(), ws.data_ptr(), wsb, dq2.data_ptr(), B, H, N, d, scale,
                              1, dt, sp)
     assert rc == _lib.FA_OK
-    d_from_dq = ws[: 4 * B * H * N].view(torch.float32).clone()
+    rows = B * H * N
+    loff = 4 * ((rows + 63) // 64 * 64)  # LSE * log2(e) starts on a 256-byte boundary
+    d_from_dq = ws[: 4 * rows].view(torch.float32).clone()
+    l_from_dq = ws[loff: loff + 4 * rows].view(torch.float32).clone()
     rc = _lib.fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
-                               lse.data_ptr(), ws.data_ptr(), wsb, dk2.data_ptr(), dv2.data_ptr(),
-                               B, H, N, d, scale, 1, dt, sp)
+                               ws.data_ptr(), wsb, dk2.data_ptr(), dv2.data_ptr(), B, H, N, d,
+                               scale, 1, dt, sp)
     assert rc == _lib.FA_OK
     for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2)):
         assert torch.equal(a, b)
-    rc = _lib.fa_backward_preprocess(o.data_ptr(), do.data_ptr(), ws.data_ptr(), wsb, B, H, N, d,
-                                     dt, sp)
+    # the standalone preprocess fills the same workspace; dK/dV from it agree
+    ws.fill_(255)
+    rc = _lib.fa_backward_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                                     wsb, B, H, N, d, dt, sp)
     assert rc == _lib.FA_OK
-    d_pre = ws[: 4 * B * H * N].view(torch.float32)
-    ref = (o.double() * do.double()).sum(-1).flatten()
+    d_pre = ws[: 4 * rows].view(torch.float32).clone()
+    l_pre = ws[loff: loff + 4 * rows].view(torch.float32).clone()
+    dk3, dv3 = torch.empty_like(q), torch.empty_like(q)
+    rc = _lib.fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                               ws.data_ptr(), wsb, dk3.data_ptr(), dv3.data_ptr(), B, H, N, d,
+                               scale, 1, dt, sp)
+    assert rc == _lib.FA_OK
     torch.cuda.synchronize()
-    assert max_abs(d_pre.cpu(), ref.cpu()) < 1e-4
-    assert max_abs(d_from_dq.cpu(), ref.cpu()) < 1e-4
+    ref = (o.double() * do.double()).sum(-1).flatten().cpu()
+    lref = (lse.double() * math.log2(math.e)).flatten().cpu()
+    assert max_abs(d_pre.cpu(), ref) < 1e-4
+    assert max_abs(d_from_dq.cpu(), ref) < 1e-4
+    assert max_abs(l_pre.cpu(), lref) < 1e-5 and max_abs(l_from_dq.cpu(), lref) < 1e-5
+    assert torch.equal(dv3, dv1)  # dV does not depend on D
+    assert rel_frob(dk3.cpu(), dk1.cpu()) < 1e-3
