@@ -34,7 +34,7 @@ namespace fa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// D_i = sum_k dO_ik O_ik  (fp32), one row per D/8 lanes (16-byte loads),
+// -D_i = -sum_k dO_ik O_ik  (fp32), one row per D/8 lanes (16-byte loads),
 // and LSE_i * log2(e) beside it.
 template <int D>
 __global__ __launch_bounds__(256)
@@ -62,7 +62,7 @@ void bwd_pre_bf16_kernel(const bf16_t* __restrict__ O, const bf16_t* __restrict_
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (row < rows && part == 0) {
-    Dws[row] = acc;
+    Dws[row] = -acc;
     Lws[row] = LSE[row] * kLog2e;
   }
 }
@@ -70,7 +70,7 @@ void bwd_pre_bf16_kernel(const bf16_t* __restrict__ O, const bf16_t* __restrict_
 // ---------------------------------------------------------------------------
 // dK, dV.  Per wavefront: 32 keys whose K and V fragments stay in VGPRs.  Per
 // step: a chunk of BQ = 32*QB query rows of Q and dO, with that chunk's
-// LSE*log2(e) and D, copied HBM -> LDS by direct buffer->LDS loads into an
+// LSE*log2(e) and -D, copied HBM -> LDS by direct buffer->LDS loads into an
 // ST-stage ring (one LDS variable per stage and operand).  Q and dO are read
 // by rows for S = Q K^T and dP = dO V^T, and through the LDS transpose unit
 // for dK^T += Q^T dS and dV^T += dO^T P.
@@ -203,10 +203,19 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       const float* ls = lst(S);
       const float* ds = dst_(S);
 
-      // S = Q K^T and dP = dO V^T (lane: key; registers: query rows).
+      // S = Q K^T and dP - D = dO V^T - D (lane: key; registers: query
+      // rows); the dP accumulator starts from the workspace's -D, register
+      // 4g + e holding row 8g + 4h + e of the block (16-byte LDS reads).
       f32x16 sacc[QB], pacc[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
+        f32x16 nd;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(ds + qb * 32 + 8 * g + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nd[4 * g + e] = v[e];
+        }
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
           const bf16x8 aq = frag_rows<D>(Qs, qb * 32, 16 * s, c32, h);
@@ -214,7 +223,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
           if (s == 0) {
             const f32x16 z = {};
             sacc[qb] = mfma32x32x16(aq, kf[s], z);
-            pacc[qb] = mfma32x32x16(ao, vf[s], z);
+            pacc[qb] = mfma32x32x16(ao, vf[s], nd);
           } else {
             sacc[qb] = mfma32x32x16(aq, kf[s], sacc[qb]);
             pacc[qb] = mfma32x32x16(ao, vf[s], pacc[qb]);
@@ -234,18 +243,29 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
           for (int e = 0; e < 4; ++e)
             sacc[qb][4 * g + e] = fast_exp2(fmaf(sacc[qb][4 * g + e], c, -lse4[e]));
         }
-      const bool need_mask = (i0 + C::BQ > N) || (CAUSAL && i0 < k0w + 31);
-      if (need_mask) {
+      const bool tail = i0 + C::BQ > N;
+      if (tail || (CAUSAL && i0 < k0w + 31)) {
         keep_branch();
         const int kqh = key - i0 - 4 * h;  // key > query  <=>  kqh > query offset
-        const int nq = N - i0 - 4 * h;     // query >= N  <=>  query offset >= nq
+        if (!tail) {
+          // causal diagonal only: one compare per entry
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+          for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
-            if ((CAUSAL && kqh > qoff) || qoff >= nq) sacc[qb][r] = 0.f;
-          }
+            for (int r = 0; r < 16; ++r) {
+              const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
+              if (qoff < kqh) sacc[qb][r] = 0.f;
+            }
+        } else {
+          const int nq = N - i0 - 4 * h;  // query >= N  <=>  query offset >= nq
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
+              if ((CAUSAL && kqh > qoff) || qoff >= nq) sacc[qb][r] = 0.f;
+            }
+        }
       }
       // dS = P (dP - D); P and dS packed to bf16 as B operands (k-step
       // u = 2*qb + (g>>1) holds registers 8*(g&1) .. of block qb).
@@ -254,10 +274,9 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 dd4 = *reinterpret_cast<const f32x4*>(ds + qb * 32 + 8 * g + 4 * h);
           float dsv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dsv[e] = sacc[qb][4 * g + e] * (pacc[qb][4 * g + e] - dd4[e]);
+          for (int e = 0; e < 4; ++e) dsv[e] = sacc[qb][4 * g + e] * pacc[qb][4 * g + e];
           const int u = 2 * qb + (g >> 1), w0 = 2 * (g & 1);
           pw[u][w0] = pack_bf16x2(sacc[qb][4 * g], sacc[qb][4 * g + 1]);
           pw[u][w0 + 1] = pack_bf16x2(sacc[qb][4 * g + 2], sacc[qb][4 * g + 3]);
@@ -398,7 +417,7 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
         for (int e = 0; e < 8; ++e) part = fmaf((float)of[rb][s][e], (float)ov[s][e], part);
       dd[rb] = sum_halves(part);
       if (h == 0 && query < N) {
-        Dws[(size_t)bh * N + query] = dd[rb];
+        Dws[(size_t)bh * N + query] = -dd[rb];
         Lws[(size_t)bh * N + query] = lse2[rb];
       }
     }
@@ -472,13 +491,16 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
         const int nk = N - j0 - 4 * h;  // key >= N  <=>  key offset >= nk
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          const int kq = j0 + 4 * h - (q0w + 32 * rb + c32);  // key - query = kq + key offset
+          // key - query = kq + key offset; future keys and keys past the end
+          // both have key offset > lim
+          const int kq = j0 + 4 * h - (q0w + 32 * rb + c32);
+          const int lim = CAUSAL ? min(-kq, nk - 1) : nk - 1;
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
-              if ((CAUSAL && kq + koff > 0) || koff >= nk) sacc[rb][kb][r] = 0.f;
+              if (koff > lim) sacc[rb][kb][r] = 0.f;
             }
         }
       }
@@ -546,7 +568,7 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
   const int BH = p.B * p.H;
   const long long rows = (long long)BH * p.N;
   const float c = p.scale * kLog2e;
-  float* Dws = ws;         // D, one float per row
+  float* Dws = ws;         // -D, one float per row
   float* Lws = ws + ws_lse_offset(rows);  // LSE * log2(e), one float per row
   if (stages & kStagePre) {
     constexpr int RPB = 256 / (D / 8);

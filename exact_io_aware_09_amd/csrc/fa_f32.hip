@@ -130,7 +130,7 @@ void bwd_pre_f32_kernel(const float* __restrict__ O, const float* __restrict__ d
   for (int e = 0; e < 16; ++e) acc = fmaf(a[e], b[e], acc);
   acc = group_sum<TPR>(acc);
   if (ok && part == 0) {
-    Dws[row] = acc;
+    Dws[row] = -acc;
     Lws[row] = LSE[row] * kLog2e;
   }
 }
@@ -164,7 +164,7 @@ void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     if (threadIdx.x < kTile) {
       const int r = i0 + threadIdx.x;
       Ls[threadIdx.x] = r < N ? Lws[(size_t)bh * N + r] : 0.f;  // LSE * log2(e)
-      Ds[threadIdx.x] = r < N ? Dws[(size_t)bh * N + r] : 0.f;
+      Ds[threadIdx.x] = r < N ? -Dws[(size_t)bh * N + r] : 0.f;  // the workspace holds -D
     }
     __syncthreads();
     for (int i = 0; i < kTile; ++i) {
@@ -219,7 +219,7 @@ void bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 #pragma unroll
   for (int e = 0; e < 16; ++e) dq[e] = 0.f;
   const float lse = ok ? LSE[(size_t)bh * N + row] : 0.f;
-  const float dd = ok ? Dws[(size_t)bh * N + row] : 0.f;
+  const float dd = ok ? -Dws[(size_t)bh * N + row] : 0.f;  // the workspace holds -D
   const int kend = CAUSAL ? min(N, q0 + RPB) : N;
   for (int j0 = 0; j0 < kend; j0 += kTile) {
     __syncthreads();
@@ -270,7 +270,7 @@ hipError_t run_bwd_f32(const float* Q, const float* K, const float* V, const flo
                        float* ws, const Problem& p, unsigned stages, hipStream_t stream) {
   constexpr int RPB = 256 / (D / 16);
   const long long rows = (long long)p.B * p.H * p.N;
-  float* Dws = ws;         // D, one float per row
+  float* Dws = ws;         // -D, one float per row
   float* Lws = ws + ws_lse_offset(rows);  // LSE * log2(e), one float per row
   const long long gpre = (rows + RPB - 1) / RPB;
   const int nb = (p.N + RPB - 1) / RPB;

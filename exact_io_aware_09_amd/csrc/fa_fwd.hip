@@ -171,13 +171,16 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
         const int nk = N - j0 - 4 * h;  // key >= N  <=>  key offset >= nk
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
+          // key - query = kq + key offset; future keys and keys past the end
+          // both have key offset > lim
           const int kq = j0 + 4 * h - (q0w + 32 * rb + c32);
+          const int lim = CAUSAL ? min(-kq, nk - 1) : nk - 1;
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
-              if ((CAUSAL && kq + koff > 0) || koff >= nk) sacc[rb][kb][r] = -INFINITY;
+              if (koff > lim) sacc[rb][kb][r] = -INFINITY;
             }
         }
       }

@@ -13,7 +13,7 @@ struct Problem {
 // bfloat16 inputs, fp32 accumulation on the matrix cores.
 hipError_t launch_forward_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                const Problem& p, hipStream_t stream);
-// Backward workspace: D (one float per query row), then, starting at float
+// Backward workspace: -D (one float per query row), then, starting at float
 // index ws_lse_offset(rows), LSE * log2(e) (one float per row).
 inline long long ws_lse_offset(long long rows) { return (rows + 63) & ~63LL; }
 

@@ -80,7 +80,8 @@ int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
 /*
  * Bytes of device workspace fa_backward needs: two float32 vectors of one
  * value per query row (B*H*N rows), each starting on a 256-byte boundary --
- * D_i = sum_k dO_ik O_ik (the vector of CS324 notes section 5.4) and
+ * -D_i = -sum_k dO_ik O_ik (D is the vector of CS324 notes section 5.4;
+ * stored negated so that it can start the dP accumulation) and
  * LSE_i * log2(e).  Returns 0 for invalid sizes.
  */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype);
@@ -89,7 +90,7 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype);
  * Backward pass.  Reads Q, K, V, O, dO and the forward's LSE; writes dQ, dK,
  * dV (all [B,H,N,d], dtype) completely (no accumulation into the caller's
  * buffers).  `workspace` (device memory of at least
- * fa_backward_workspace_bytes(), contents ignored on entry) receives D and
+ * fa_backward_workspace_bytes(), contents ignored on entry) receives -D and
  * LSE * log2(e).  Two kernels are enqueued on `stream`, in order: a dQ
  * kernel (one Q block per workgroup, loop over K/V blocks) that also forms
  * D = rowsum(dO * O) and LSE * log2(e) for its rows and stores them in
@@ -109,7 +110,7 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O,
  * fa_backward_dkdv on one stream computes exactly what fa_backward computes
  * (the same kernels, bit for bit).
  *
- * fa_backward_dq:   reads Q, K, V, O, dO and LSE; writes dQ, and writes D
+ * fa_backward_dq:   reads Q, K, V, O, dO and LSE; writes dQ, and writes -D
  *   (D_i = sum_k dO_ik O_ik, float32: the identity of CS324 notes section
  *   5.4 that replaces sum_j P_ij dP_ij) and LSE * log2(e) into `workspace`.
  * fa_backward_dkdv: reads Q, K, V, dO and the two workspace vectors; writes
