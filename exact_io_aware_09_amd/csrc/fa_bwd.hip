@@ -90,17 +90,6 @@ struct DkdvCfg {
   static_assert(ST >= 2 && ST <= 3, "two or three Q/dO stages");
 };
 
-// Copies `rows` consecutive floats starting at row r0 of a per-head float
-// vector into LDS (lane L -> dst[L], rows past the vector's end read as 0).
-// Every wavefront issues the same copy: the writes are identical, so any
-// wavefront's own wait makes the data visible to it.
-template <int ROWS>
-__device__ __forceinline__ void dma_rows_f32(__amdgpu_buffer_rsrc_t r, int r0, float* dst, int lane) {
-  typedef __attribute__((address_space(3))) void* lds_void_ptr;
-  const uint32_t goff = (uint32_t)(r0 + (lane % ROWS)) * 4u;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)dst, 4, goff, 0, 0, 0);
-}
-
 template <int D, int NW, int QB, int ST, int OCC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
@@ -142,27 +131,14 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   grouped_order(xcd_remap(blockIdx.x, BH * nkb), nkb, BH, G, bh, kb);
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const auto rq = make_rsrc(Q + hoff, head_bytes);
-  const auto ro = make_rsrc(dO + hoff, head_bytes);
-  const auto rl = make_rsrc(Lws + (size_t)bh * N, (uint32_t)N * 4u);
-  const auto rd = make_rsrc(Dws + (size_t)bh * N, (uint32_t)N * 4u);
+  const auto rq = make_copy_rsrc(Q + hoff, head_bytes);
+  const auto ro = make_copy_rsrc(dO + hoff, head_bytes);
+  const auto rl = make_copy_rsrc(Lws + (size_t)bh * N, (uint32_t)N * 4u);
+  const auto rd = make_copy_rsrc(Dws + (size_t)bh * N, (uint32_t)N * 4u);
 
   const int k0 = kb * C::BK;
   const int k0w = k0 + w * 32;
   const int key = k0w + c32;  // this lane's key row (MFMA column)
-
-  // K and V fragments: B operands of S = Q K^T and dP = dO V^T (lane = key).
-  bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
-  {
-    const auto rk = make_rsrc(K + hoff, head_bytes);
-    const auto rv = make_rsrc(V + hoff, head_bytes);
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
-      const uint32_t off = ((uint32_t)key * D + 16 * s + 8 * h) * 2u;
-      kf[s] = as_bf16x8(buf_load16(rk, off));
-      vf[s] = as_bf16x8(buf_load16(rv, off));
-    }
-  }
 
   f32x16 dkacc[C::DB], dvacc[C::DB];
 #pragma unroll
@@ -183,13 +159,36 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     dma_rows_f32<C::BQ>(rl, i0, lst(S), lane);
     dma_rows_f32<C::BQ>(rd, i0, dst_(S), lane);
   };
-  wait_vmem_all();  // K and V fragments are in registers before the copies start
+  // The first Q/dO copies go out before the K/V loads, so that both
+  // latencies overlap.
   fetch(0, std::integral_constant<int, 0>{});
   if constexpr (ST > 2) {
     if (1 < nchunks) fetch(1, std::integral_constant<int, 1>{});
   }
+
+  // K and V fragments: B operands of S = Q K^T and dP = dO V^T (lane = key).
+  bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
+  {
+    const auto rk = make_rsrc(K + hoff, head_bytes);
+    const auto rv = make_rsrc(V + hoff, head_bytes);
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) {
+      const uint32_t off = ((uint32_t)key * D + 16 * s + 8 * h) * 2u;
+      kf[s] = as_bf16x8(buf_load16(rk, off));
+      vf[s] = as_bf16x8(buf_load16(rv, off));
+    }
+  }
+
+  // K and V resident here: the compiler does not count the copies, so its
+  // own waits for K and V must not fall inside the loop (where they would
+  // also drain the copies in flight).
+#pragma unroll
+  for (int s = 0; s < C::KSTEPS; ++s) {
+    pin_ready(kf[s]);
+    pin_ready(vf[s]);
+  }
   wait_vmem_tiles<C::DMA_PER_TILE, ST - 2>(min(ST - 2, nchunks - 1));
-  __syncthreads();
+  ring_barrier();
 
   auto step = [&](int t, auto S) {
     constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
@@ -299,7 +298,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     // step t+1 must be resident; later steps may still be in flight
     if (t + 1 < nchunks) {
       wait_vmem_tiles<C::DMA_PER_TILE, ST - 2>(min(ST - 2, nchunks - t - 2));
-      __syncthreads();
+      ring_barrier();
     }
   };
   for (int t0 = 0; t0 < nchunks; t0 += ST) {
@@ -382,11 +381,33 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
   const int qb = CAUSAL ? (nqb - 1 - rank) : rank;  // longest causal blocks first
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const auto rk = make_rsrc(K + hoff, head_bytes);
-  const auto rv = make_rsrc(V + hoff, head_bytes);
+  const auto rk = make_copy_rsrc(K + hoff, head_bytes);
+  const auto rv = make_copy_rsrc(V + hoff, head_bytes);
 
   const int q0 = qb * C::BR;
   const int q0w = q0 + w * C::RW;  // row block rb of this lane: query q0w + 32 rb + c32
+
+  f32x16 dqacc[RB][C::DB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqacc[rb][db][r] = 0.f;
+
+  const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+
+  auto fetch = [&](int t, auto S) {
+    dma_tile<D, BC, C::NT>(rk, t * BC, kst(S), tid);
+    dma_tile<D, BC, C::NT>(rv, t * BC, vst(S), tid);
+  };
+  // The first K/V copies go out before the Q, dO and O loads, so that both
+  // latencies overlap.
+  fetch(0, std::integral_constant<int, 0>{});
+  if constexpr (ST > 2) {
+    if (1 < ntiles) fetch(1, std::integral_constant<int, 1>{});
+  }
 
   // Q and dO fragments (B operands, lane = query row: half h holds head dims
   // 16s + 8h .. +7), LSE in log2 units, and D_i = sum_k dO_ik O_ik formed
@@ -423,28 +444,18 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
     }
   }
 
-  f32x16 dqacc[RB][C::DB];
+  // Q and dO resident here: the compiler does not count the copies, so its
+  // own waits for them must not fall inside the loop (where they would also
+  // drain the copies in flight).
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dqacc[rb][db][r] = 0.f;
-
-  const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
-  const int ntiles = (kend + BC - 1) / BC;
-
-  auto fetch = [&](int t, auto S) {
-    dma_tile<D, BC, C::NT>(rk, t * BC, kst(S), tid);
-    dma_tile<D, BC, C::NT>(rv, t * BC, vst(S), tid);
-  };
-  wait_vmem_all();  // Q, dO, O, LSE are in registers before the copies start
-  fetch(0, std::integral_constant<int, 0>{});
-  if constexpr (ST > 2) {
-    if (1 < ntiles) fetch(1, std::integral_constant<int, 1>{});
-  }
+    for (int s = 0; s < C::KSTEPS; ++s) {
+      pin_ready(qf[rb][s]);
+      pin_ready(of[rb][s]);
+    }
   wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - 1));
-  __syncthreads();
+  ring_barrier();
 
   auto step = [&](int t, auto S) {
     constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
@@ -531,7 +542,7 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
     // step t+1 must be resident; later steps may still be in flight
     if (t + 1 < ntiles) {
       wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - t - 2));
-      __syncthreads();
+      ring_barrier();
     }
   };
   for (int t0 = 0; t0 < ntiles; t0 += ST) {

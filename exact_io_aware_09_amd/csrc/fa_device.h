@@ -215,19 +215,84 @@ __device__ __forceinline__ bf16x8 bf16x8_from(uint32_t a, uint32_t b, uint32_t c
   return __builtin_bit_cast(bf16x8, make_uint4(a, b, c, d));
 }
 
-// Direct global -> LDS copy of one [ROWS x D] bf16 block (rows r0.. of the
-// buffer resource's tensor) into a swizzled LDS tile, without VGPRs.  Each
-// wavefront instruction writes 64 x 16 bytes to consecutive LDS addresses
-// (lane L at base + 16 L, base wave-uniform), so lane L fetches the global
-// chunk that the swizzle places at that position.  Rows past the end of the
-// resource read as zeros.  Completion is tracked by the vector-memory counter.
+// Workgroup barrier for the LDS rings.  Every wavefront first waits for its
+// own LDS reads (lgkmcnt 0) and, before calling this, for its own copies of
+// the next block (explicit vmcnt wait); after the barrier the block is
+// complete and no wavefront still reads the stage that the next copies
+// overwrite.  Unlike __syncthreads() this does not also drain the copies of
+// later blocks still in flight (a workgroup-scope release fence would wait
+// for every outstanding load).  The asm statement is also a compiler barrier
+// for memory accesses.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS copies (buffer_load ... lds).  They are issued from
+// inline assembly so that the compiler does not track them: otherwise it
+// waits for every copy in flight before any later LDS read it cannot prove
+// disjoint, which would serialise the ring of stages.  Completion is
+// awaited explicitly (s_waitcnt vmcnt, then ring_barrier) before a block is
+// read.  M0 (the LDS base of the wavefront) is saved and restored around
+// each copy, and the copy waits one cycle after M0 is written.
+typedef int copy_rsrc __attribute__((ext_vector_type(4)));  // buffer descriptor words
+
+// Descriptor over `bytes` bytes at `base` (stride 0, raw buffer); reads at
+// or beyond `bytes` return zeros.  Same fields as make_rsrc.
+__device__ __forceinline__ copy_rsrc make_copy_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  copy_rsrc r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p));
+}
+
+// Lane L copies 16 bytes at byte offset voff to LDS address lds + 16 L.
+__device__ __forceinline__ void lds_copy16(copy_rsrc r, uint32_t voff, uint32_t lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory");
+}
+
+// Lane L copies 4 bytes at byte offset voff to LDS address lds + 4 L.
+__device__ __forceinline__ void lds_copy4(copy_rsrc r, uint32_t voff, uint32_t lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory");
+}
+
+// Copy of one [ROWS x D] bf16 block (rows r0.. of the descriptor's tensor)
+// into a swizzled LDS tile, without VGPRs.  Each wavefront instruction
+// writes 64 x 16 bytes to consecutive LDS addresses, so lane L fetches the
+// global chunk that the swizzle places at that position.  Rows past the end
+// of the descriptor read as zeros.  CHUNKS / NT copies per lane.
 template <int D, int ROWS, int NT>
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, int r0, bf16_t* tile, int tid) {
+__device__ __forceinline__ void dma_tile(copy_rsrc r, int r0, bf16_t* tile, int tid) {
   constexpr int CPR = D / 8;               // chunks per row
   constexpr int CHUNKS = ROWS * CPR;
   constexpr int NWAVE = NT / kWave;
   static_assert(CHUNKS % NT == 0, "block must split evenly over the threads");
-  typedef __attribute__((address_space(3))) void* lds_void_ptr;
   const int w = tid >> 6, lane = tid & 63;
 #pragma unroll
   for (int i = 0; i < CHUNKS / NT; ++i) {
@@ -235,8 +300,18 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, int r0, bf16_
     const int pos = blk * 64 + lane;         // chunk position in LDS
     const int row = pos / CPR, c = (pos % CPR) ^ swz<D>(row);
     const uint32_t goff = ((uint32_t)(r0 + row) * D + c * 8) * 2u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(tile + blk * 512), 16, goff, 0, 0, 0);
+    lds_copy16(r, goff, lds_address(tile + blk * 512));
   }
+}
+
+// Copy of `ROWS` (<= 64) consecutive floats starting at row r0 of a float
+// vector into LDS (lane L -> dst[L]; lanes past ROWS repeat rows, so dst
+// must hold 64 floats; rows past the descriptor's end read as 0).  One copy
+// per lane.
+template <int ROWS>
+__device__ __forceinline__ void dma_rows_f32(copy_rsrc r, int r0, float* dst, int lane) {
+  static_assert(ROWS <= kWave, "one lane per row");
+  lds_copy4(r, (uint32_t)(r0 + (lane % ROWS)) * 4u, lds_address(dst));
 }
 
 // Scheduling hints: ask the compiler's scheduler to interleave instruction
@@ -256,6 +331,13 @@ __device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float c) {
 // not execute an asm statement speculatively, so it cannot if-convert the
 // block into selects evaluated on every iteration.
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
+
+// Makes the value's registers an input of an empty volatile asm statement:
+// the loads producing it complete (the compiler waits for them) before this
+// point, and volatile asm statements keep their order, so those loads are
+// not scheduled after the untracked LDS copies issued later.
+template <typename T>
+__device__ __forceinline__ void pin_ready(const T& x) { asm volatile("" ::"v"(x)); }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 

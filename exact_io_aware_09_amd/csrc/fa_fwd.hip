@@ -56,6 +56,9 @@ struct FwdCfg {
   static constexpr int KB = BC / 32;           // 32-key blocks per tile
   static constexpr int PU = BC / 16;           // k-steps of V^T P^T
   static constexpr int DMA_PER_TILE = TILE / 8 / NT;  // loads per tile per lane
+  // Q block staged through LDS (coalesced copy in, O out through the same
+  // rows) when it fits in 16 KB; otherwise Q fragments load straight from HBM
+  static constexpr bool QL = BR * D * 2 <= 16384;
   static_assert(ST >= 2 && ST <= 3, "two or three K/V stages");
 };
 
@@ -76,6 +79,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   __shared__ __attribute__((aligned(16))) bf16_t k0s[C::TILE], v0s[C::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t k1s[ST > 1 ? C::TILE : 8], v1s[ST > 1 ? C::TILE : 8];
   __shared__ __attribute__((aligned(16))) bf16_t k2s[ST > 2 ? C::TILE : 8], v2s[ST > 2 ? C::TILE : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t qs[C::QL ? C::BR * D : 8];
   auto kst = [&](auto S) -> bf16_t* {
     if constexpr (decltype(S)::value == 0) return k0s;
     else if constexpr (decltype(S)::value == 1) return k1s;
@@ -93,22 +97,12 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   const int qb = CAUSAL ? (nqb - 1 - rank) : rank;  // longest causal blocks first
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const auto rq = make_rsrc(Q + hoff, head_bytes);
-  const auto rk = make_rsrc(K + hoff, head_bytes);
-  const auto rv = make_rsrc(V + hoff, head_bytes);
+  const auto rk = make_copy_rsrc(K + hoff, head_bytes);
+  const auto rv = make_copy_rsrc(V + hoff, head_bytes);
 
   const int q0 = qb * C::BR;
   const int q0w = q0 + w * C::RW;  // first query row of this wavefront
   // this lane's query row in row block rb is q0w + 32 * rb + c32
-
-  // Query fragments: B operands of S^T = K Q^T (lane = query row).
-  bf16x8 qf[RB][C::KSTEPS];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s)
-      qf[rb][s] = as_bf16x8(
-          buf_load16(rq, ((uint32_t)(q0w + 32 * rb + c32) * D + 16 * s + 8 * h) * 2u));
 
   const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
@@ -117,12 +111,42 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     dma_tile<D, BC, C::NT>(rk, t * BC, kst(S), tid);
     dma_tile<D, BC, C::NT>(rv, t * BC, vst(S), tid);
   };
+  // The first K/V copies go out before Q is read, so that the latencies
+  // overlap.
   fetch(0, std::integral_constant<int, 0>{});
+  bf16x8 qf[RB][C::KSTEPS];  // B operands of S^T = K Q^T (lane = query row)
+  if constexpr (C::QL) {
+    // Q block copied row-major (coalesced) into LDS, rows past N as zeros
+    dma_tile<D, C::BR, C::NT>(make_copy_rsrc(Q + hoff, head_bytes), q0, qs, tid);
+  } else {
+    const auto rq = make_rsrc(Q + hoff, head_bytes);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s)
+        qf[rb][s] = as_bf16x8(
+            buf_load16(rq, ((uint32_t)(q0w + 32 * rb + c32) * D + 16 * s + 8 * h) * 2u));
+    // Q resident here: the compiler does not count the copies, so its own
+    // waits for Q must not fall inside the loop (where they would also
+    // drain the copies in flight).
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) pin_ready(qf[rb][s]);
+  }
   if constexpr (ST > 2) {
     if (1 < ntiles) fetch(1, std::integral_constant<int, 1>{});
   }
   wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - 1));
-  __syncthreads();
+  ring_barrier();
+  if constexpr (C::QL) {
+    // each wavefront reads (and later overwrites with O) only its own rows
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s)
+        qf[rb][s] = frag_rows<D>(qs, w * C::RW + 32 * rb, 16 * s, c32, h);
+  }
 
   f32x16 oacc[RB][C::DB];
   float m[RB], l[RB];
@@ -241,7 +265,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     // step t+1 must be resident; later steps may still be in flight
     if (t + 1 < ntiles) {
       wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - t - 2));
-      __syncthreads();
+      ring_barrier();
     }
   };
   for (int t0 = 0; t0 < ntiles; t0 += ST) {
@@ -258,7 +282,19 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     const int query = q0w + 32 * rb + c32;
     const float lt = sum_halves(l[rb]);
     const float inv = 1.f / lt;
-    if (query < N) {
+    if constexpr (C::QL) {
+      // O fragment (dims db*32 + 8g + 4h + 0..3 of this lane's row) into
+      // this wavefront's rows of the Q staging tile
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t lo = pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv);
+          const uint32_t hi = pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(qs + tile_off<D>(w * C::RW + 32 * rb + c32, db * 32 + 8 * g + 4 * h)) =
+              make_uint2(lo, hi);
+        }
+    } else if (query < N) {
       bf16_t* Or = O + hoff + (size_t)query * D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -268,7 +304,19 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
           const uint32_t hi = pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
           *reinterpret_cast<uint2*>(Or + db * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
         }
-      if (h == 0) LSE[(size_t)bh * N + query] = fmaf(m[rb], kLn2, logf(lt));
+    }
+    if (h == 0 && query < N) LSE[(size_t)bh * N + query] = fmaf(m[rb], kLn2, logf(lt));
+  }
+  if constexpr (C::QL) {
+    // rows back out of LDS as whole 16-byte chunks: 8 lanes per row, so each
+    // store instruction writes 8 complete rows
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int i = 0; i < C::RW * CPR / kWave; ++i) {
+      const int chunk = i * kWave + lane;
+      const int r = chunk / CPR, cc = chunk % CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(qs + tile_off<D>(w * C::RW + r, cc * 8));
+      if (q0w + r < N) *reinterpret_cast<uint4*>(O + hoff + (size_t)(q0w + r) * D + cc * 8) = v;
     }
   }
 }
