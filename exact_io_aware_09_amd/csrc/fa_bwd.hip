@@ -86,6 +86,10 @@ struct DkdvCfg {
   // per stage and wavefront: Q and dO tiles, then one 4-byte copy each of
   // the chunk's LSE*log2e and D
   static constexpr int DMA_PER_TILE = 2 * (TILE / 8 / NT) + 2;
+  // K and V blocks staged through LDS (coalesced copies in, dK and dV out
+  // through the same rows) when both fit in 32 KB; otherwise their
+  // fragments load straight from HBM
+  static constexpr bool KL = 2 * BK * D * 2 <= 32768;
   static_assert(BQ <= kWave, "one lane per chunk row copies LSE and D");
   static_assert(ST >= 2 && ST <= 3, "two or three Q/dO stages");
 };
@@ -104,6 +108,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   __shared__ __attribute__((aligned(16))) bf16_t q2s[ST > 2 ? C::TILE : 8], o2s[ST > 2 ? C::TILE : 8];
   __shared__ __attribute__((aligned(16))) float l0s[kWave], d0s[kWave], l1s[kWave], d1s[kWave];
   __shared__ __attribute__((aligned(16))) float l2s[ST > 2 ? kWave : 4], d2s[ST > 2 ? kWave : 4];
+  __shared__ __attribute__((aligned(16))) bf16_t ksg[C::KL ? C::BK * D : 8], vsg[C::KL ? C::BK * D : 8];
   auto qst = [&](auto S) -> bf16_t* {
     if constexpr (decltype(S)::value == 0) return q0s;
     else if constexpr (decltype(S)::value == 1) return q1s;
@@ -159,16 +164,16 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     dma_rows_f32<C::BQ>(rl, i0, lst(S), lane);
     dma_rows_f32<C::BQ>(rd, i0, dst_(S), lane);
   };
-  // The first Q/dO copies go out before the K/V loads, so that both
+  // The first Q/dO copies go out before K and V are read, so that the
   // latencies overlap.
   fetch(0, std::integral_constant<int, 0>{});
-  if constexpr (ST > 2) {
-    if (1 < nchunks) fetch(1, std::integral_constant<int, 1>{});
-  }
-
   // K and V fragments: B operands of S = Q K^T and dP = dO V^T (lane = key).
   bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
-  {
+  if constexpr (C::KL) {
+    // K and V blocks copied row-major (coalesced) into LDS, rows past N as 0
+    dma_tile<D, C::BK, C::NT>(make_copy_rsrc(K + hoff, head_bytes), k0, ksg, tid);
+    dma_tile<D, C::BK, C::NT>(make_copy_rsrc(V + hoff, head_bytes), k0, vsg, tid);
+  } else {
     const auto rk = make_rsrc(K + hoff, head_bytes);
     const auto rv = make_rsrc(V + hoff, head_bytes);
 #pragma unroll
@@ -177,18 +182,28 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       kf[s] = as_bf16x8(buf_load16(rk, off));
       vf[s] = as_bf16x8(buf_load16(rv, off));
     }
-  }
-
-  // K and V resident here: the compiler does not count the copies, so its
-  // own waits for K and V must not fall inside the loop (where they would
-  // also drain the copies in flight).
+    // K and V resident here: the compiler does not count the copies, so its
+    // own waits for K and V must not fall inside the loop (where they would
+    // also drain the copies in flight).
 #pragma unroll
-  for (int s = 0; s < C::KSTEPS; ++s) {
-    pin_ready(kf[s]);
-    pin_ready(vf[s]);
+    for (int s = 0; s < C::KSTEPS; ++s) {
+      pin_ready(kf[s]);
+      pin_ready(vf[s]);
+    }
+  }
+  if constexpr (ST > 2) {
+    if (1 < nchunks) fetch(1, std::integral_constant<int, 1>{});
   }
   wait_vmem_tiles<C::DMA_PER_TILE, ST - 2>(min(ST - 2, nchunks - 1));
   ring_barrier();
+  if constexpr (C::KL) {
+    // each wavefront reads (and later overwrites with dK, dV) only its rows
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) {
+      kf[s] = frag_rows<D>(ksg, w * 32, 16 * s, c32, h);
+      vf[s] = frag_rows<D>(vsg, w * 32, 16 * s, c32, h);
+    }
+  }
 
   auto step = [&](int t, auto S) {
     constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
@@ -309,7 +324,40 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     }
   }
 
-  if (key < N) {
+  if constexpr (C::KL) {
+    // fragments (dims db*32 + 8g + 4h + 0..3 of this lane's key row) into
+    // this wavefront's rows of the staging tiles, then out as whole rows:
+    // 8 lanes per row, each store instruction writes 8 complete rows
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<uint2*>(ksg + tile_off<D>(w * 32 + c32, db * 32 + 8 * g + 4 * h)) =
+            make_uint2(pack_bf16x2(dkacc[db][4 * g] * scale, dkacc[db][4 * g + 1] * scale),
+                       pack_bf16x2(dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale));
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / kWave; ++i) {
+      const int chunk = i * kWave + lane;
+      const int r = chunk / CPR, cc = chunk % CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(ksg + tile_off<D>(w * 32 + r, cc * 8));
+      if (k0w + r < N) *reinterpret_cast<uint4*>(dK + hoff + (size_t)(k0w + r) * D + cc * 8) = v;
+    }
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<uint2*>(vsg + tile_off<D>(w * 32 + c32, db * 32 + 8 * g + 4 * h)) =
+            make_uint2(pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]),
+                       pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]));
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / kWave; ++i) {
+      const int chunk = i * kWave + lane;
+      const int r = chunk / CPR, cc = chunk % CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(vsg + tile_off<D>(w * 32 + r, cc * 8));
+      if (k0w + r < N) *reinterpret_cast<uint4*>(dV + hoff + (size_t)(k0w + r) * D + cc * 8) = v;
+    }
+  } else if (key < N) {
     bf16_t* dKr = dK + hoff + (size_t)key * D;
     bf16_t* dVr = dV + hoff + (size_t)key * D;
 #pragma unroll
@@ -349,6 +397,10 @@ struct DqCfg {
   static constexpr int KB = BC / 32;
   static constexpr int PU = BC / 16;
   static constexpr int DMA_PER_TILE = TILE / 8 / NT;
+  // Q and dO blocks staged through LDS (coalesced copies in, dQ out through
+  // the Q rows) when both fit in 32 KB; otherwise their fragments load
+  // straight from HBM
+  static constexpr bool QL = 2 * BR * D * 2 <= 32768;
   static_assert(ST >= 2 && ST <= 3, "two or three K/V stages");
 };
 
@@ -363,6 +415,7 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
   __shared__ __attribute__((aligned(16))) bf16_t k0s[C::TILE], v0s[C::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t k1s[C::TILE], v1s[C::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t k2s[ST > 2 ? C::TILE : 8], v2s[ST > 2 ? C::TILE : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t qsg[C::QL ? C::BR * D : 8], osg[C::QL ? C::BR * D : 8];
   auto kst = [&](auto S) -> bf16_t* {
     if constexpr (decltype(S)::value == 0) return k0s;
     else if constexpr (decltype(S)::value == 1) return k1s;
@@ -402,17 +455,23 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
     dma_tile<D, BC, C::NT>(rk, t * BC, kst(S), tid);
     dma_tile<D, BC, C::NT>(rv, t * BC, vst(S), tid);
   };
-  // The first K/V copies go out before the Q, dO and O loads, so that both
+  // The first K/V copies go out before Q, dO and O are read, so that the
   // latencies overlap.
   fetch(0, std::integral_constant<int, 0>{});
+  if constexpr (C::QL) {
+    // Q and dO blocks copied row-major (coalesced) into LDS, rows past N as 0
+    dma_tile<D, C::BR, C::NT>(make_copy_rsrc(Q + hoff, head_bytes), q0, qsg, tid);
+    dma_tile<D, C::BR, C::NT>(make_copy_rsrc(dO + hoff, head_bytes), q0, osg, tid);
+  }
   if constexpr (ST > 2) {
     if (1 < ntiles) fetch(1, std::integral_constant<int, 1>{});
   }
 
   // Q and dO fragments (B operands, lane = query row: half h holds head dims
   // 16s + 8h .. +7), LSE in log2 units, and D_i = sum_k dO_ik O_ik formed
-  // here from the matching O fragment and stored for the dK/dV kernel.
-  bf16x8 qf[RB][C::KSTEPS], of[RB][C::KSTEPS];
+  // here from the matching O fragment (read once, straight from HBM) and
+  // stored for the dK/dV kernel.
+  bf16x8 qf[RB][C::KSTEPS], of[RB][C::KSTEPS], ov[RB][C::KSTEPS];
   float lse2[RB], dd[RB];
   {
     const auto rq = make_rsrc(Q + hoff, head_bytes);
@@ -422,28 +481,44 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int query = q0w + 32 * rb + c32;
-      bf16x8 ov[C::KSTEPS];
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         const uint32_t off = ((uint32_t)query * D + 16 * s + 8 * h) * 2u;
-        qf[rb][s] = as_bf16x8(buf_load16(rq, off));
-        of[rb][s] = as_bf16x8(buf_load16(ro, off));
-        ov[s] = as_bf16x8(buf_load16(rO, off));
+        if constexpr (!C::QL) {
+          qf[rb][s] = as_bf16x8(buf_load16(rq, off));
+          of[rb][s] = as_bf16x8(buf_load16(ro, off));
+        }
+        ov[rb][s] = as_bf16x8(buf_load16(rO, off));
       }
       lse2[rb] = buf_load_f32(rl, (uint32_t)query * 4u) * kLog2e;
-      float part = 0.f;
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part = fmaf((float)of[rb][s][e], (float)ov[s][e], part);
-      dd[rb] = sum_halves(part);
-      if (h == 0 && query < N) {
-        Dws[(size_t)bh * N + query] = -dd[rb];
-        Lws[(size_t)bh * N + query] = lse2[rb];
-      }
     }
   }
-
+  wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - 1));
+  ring_barrier();
+  if constexpr (C::QL) {
+    // each wavefront reads (and later overwrites with dQ) only its own rows
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        qf[rb][s] = frag_rows<D>(qsg, w * C::RW + 32 * rb, 16 * s, c32, h);
+        of[rb][s] = frag_rows<D>(osg, w * C::RW + 32 * rb, 16 * s, c32, h);
+      }
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int query = q0w + 32 * rb + c32;
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)of[rb][s][e], (float)ov[rb][s][e], part);
+    dd[rb] = sum_halves(part);
+    if (h == 0 && query < N) {
+      Dws[(size_t)bh * N + query] = -dd[rb];
+      Lws[(size_t)bh * N + query] = lse2[rb];
+    }
+  }
   // Q and dO resident here: the compiler does not count the copies, so its
   // own waits for them must not fall inside the loop (where they would also
   // drain the copies in flight).
@@ -454,8 +529,6 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
       pin_ready(qf[rb][s]);
       pin_ready(of[rb][s]);
     }
-  wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - 1));
-  ring_barrier();
 
   auto step = [&](int t, auto S) {
     constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
@@ -553,20 +626,43 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
     }
   }
 
+  if constexpr (C::QL) {
+    // fragments (dims db*32 + 8g + 4h + 0..3 of this lane's row) into this
+    // wavefront's rows of the Q staging tile, then out as whole rows: 8 lanes
+    // per row, each store instruction writes 8 complete rows
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int query = q0w + 32 * rb + c32;
-    if (query < N) {
-      bf16_t* dQr = dQ + hoff + (size_t)query * D;
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 v;
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint2*>(qsg + tile_off<D>(w * C::RW + 32 * rb + c32, db * 32 + 8 * g + 4 * h)) =
+              make_uint2(pack_bf16x2(dqacc[rb][db][4 * g] * scale, dqacc[rb][db][4 * g + 1] * scale),
+                         pack_bf16x2(dqacc[rb][db][4 * g + 2] * scale, dqacc[rb][db][4 * g + 3] * scale));
+    constexpr int CPR = D / 8;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = to_bf16(dqacc[rb][db][4 * g + e] * scale);
-          *reinterpret_cast<bf16x4*>(dQr + db * 32 + 8 * g + 4 * h) = v;
-        }
+    for (int i = 0; i < C::RW * CPR / kWave; ++i) {
+      const int chunk = i * kWave + lane;
+      const int r = chunk / CPR, cc = chunk % CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(qsg + tile_off<D>(w * C::RW + r, cc * 8));
+      if (q0w + r < N) *reinterpret_cast<uint4*>(dQ + hoff + (size_t)(q0w + r) * D + cc * 8) = v;
+    }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int query = q0w + 32 * rb + c32;
+      if (query < N) {
+        bf16_t* dQr = dQ + hoff + (size_t)query * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = to_bf16(dqacc[rb][db][4 * g + e] * scale);
+            *reinterpret_cast<bf16x4*>(dQr + db * 32 + 8 * g + 4 * h) = v;
+          }
+      }
     }
   }
 }
@@ -624,7 +720,7 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
 // then dQ (wavefronts per workgroup, 32-row query blocks per wavefront, keys
 // per K/V block, K/V stages, minimum wavefronts per SIMD).
 #ifndef FA_BWD_CFG_D64
-#define FA_BWD_CFG_D64 4, 2, 2, 2, 4, 1, 32, 2, 3
+#define FA_BWD_CFG_D64 4, 1, 2, 2, 4, 1, 32, 2, 3
 #endif
 #ifndef FA_BWD_CFG_D128
 #define FA_BWD_CFG_D128 4, 1, 2, 1, 4, 1, 64, 2, 1
