@@ -26,11 +26,15 @@
 //    directly the B operand of O^T += V^T P^T; the row sum is taken from the
 //    fp32 values.
 //  * exp is evaluated as exp2 with scale*log2(e) folded into one FMA.  The
-//    running maximum of a row is only raised (and that row's O, l rescaled)
-//    when a block's maximum exceeds it by more than 2^8 in the exponent;
-//    otherwise the stale maximum is kept, which leaves every weight at most
-//    2^8 and the final O = acc / l unchanged (numerator and denominator share
-//    the same base).  Rows decide individually, so each row's arithmetic
+//    running maximum of a row is taken from its first block only and then
+//    kept as the base of the exponent for as long as the block row sums stay
+//    below a bound (2^16 per lane's half of a 32-key block), which the sum
+//    that the online softmax needs anyway checks for free: no per-block
+//    maximum, and O = acc / l and the log-sum-exp are unchanged because
+//    numerator and denominator share the base.  A block that breaks the
+//    bound (rare: the scores of a row must grow by more than about 2^12 in
+//    weight) is redone with its own maximum and O, l rescaled, as in the
+//    pages' update.  Rows decide individually, so each row's arithmetic
 //    depends on its own scores alone.
 //  * Workgroups are remapped so that all query blocks of a head run on one
 //    XCD (shared L2 for the re-read K/V); within a group of heads that fills
@@ -43,7 +47,7 @@
 namespace fa {
 namespace {
 
-constexpr float kRescaleSlack = 8.0f;  // log2 units: defer rescaling up to a factor 256
+constexpr float kMaxWeight = 65536.0f;  // bound on one lane's share of a block's row sum
 
 template <int D, int NW, int RB, int BC, int ST>
 struct FwdCfg {
@@ -160,6 +164,70 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     l[rb] = 0.f;
   }
 
+  // S^T = K Q^T for the block at key j0 (lane: query; registers: keys), each
+  // K fragment feeding the RB row blocks; causal-future keys and keys past
+  // the end become -inf, on the blocks that need it only.
+  auto scores = [&](const bf16_t* Ks, int j0, f32x16 (&sacc)[RB][C::KB]) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      bf16x8 kfr[C::KSTEPS];
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) kfr[s] = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
+      const f32x16 z = {};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[0], qf[rb][0], z);
+#pragma unroll
+      for (int s = 1; s < C::KSTEPS; ++s)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[s], qf[rb][s], sacc[rb][kb]);
+    }
+    const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
+    if (need_mask) {
+      keep_branch();
+      const int nk = N - j0 - 4 * h;  // key >= N  <=>  key offset >= nk
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        // key - query = kq + key offset; future keys and keys past the end
+        // both have key offset > lim
+        const int kq = j0 + 4 * h - (q0w + 32 * rb + c32);
+        const int lim = CAUSAL ? min(-kq, nk - 1) : nk - 1;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
+            if (koff > lim) sacc[rb][kb][r] = -INFINITY;
+          }
+      }
+    }
+  };
+  // Row maximum of a block, scaled to log2 units (both halves of the row).
+  auto block_max = [&](const f32x16 (&sacc)[C::KB]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    return max_halves(mx) * c;
+  };
+  // P^T = exp2(c S^T - m) in place; returns this lane's share of the row sum.
+  auto exponentiate = [&](f32x16 (&sacc)[C::KB], float mrow) {
+    float part[C::KB * 8];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c, -mrow));
+        sacc[kb][r + 1] = fast_exp2(fmaf(sacc[kb][r + 1], c, -mrow));
+        part[kb * 8 + r / 2] = sacc[kb][r] + sacc[kb][r + 1];
+      }
+#pragma unroll
+    for (int n = C::KB * 8; n > 1; n /= 2)
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
+    return part[0];
+  };
+
   auto step = [&](int t, auto S) {
     constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
     // the stage of step t-1 is free (barrier at the end of the last step)
@@ -169,90 +237,65 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     if (active) {
       const bf16_t* Ks = kst(S);
       const bf16_t* Vs = vst(S);
-
-      // S^T = K Q^T (lane: query; registers: keys); each K fragment feeds
-      // the RB row blocks.
       f32x16 sacc[RB][C::KB];
+      scores(Ks, j0, sacc);
+      // Running maximum m (log2 units): taken from a row's first block
+      // (which always holds key 0, so it is finite) and afterwards kept
+      // while every exponentiated score of the row stays below kMaxWeight;
+      // numerator and denominator share the base, so O and the
+      // log-sum-exp do not depend on when m is raised.
+      if (t == 0) {
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        bf16x8 kfr[C::KSTEPS];
-#pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) kfr[s] = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
-        const f32x16 z = {};
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[0], qf[rb][0], z);
-#pragma unroll
-        for (int s = 1; s < C::KSTEPS; ++s)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[s], qf[rb][s], sacc[rb][kb]);
+        for (int rb = 0; rb < RB; ++rb) m[rb] = block_max(sacc[rb]);
       }
-
-      // Causal diagonal and key tail: masked scores become -inf, on the
-      // blocks that need it only (key - query = kq + register offset).
-      const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
-      if (need_mask) {
-        keep_branch();
-        const int nk = N - j0 - 4 * h;  // key >= N  <=>  key offset >= nk
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          // key - query = kq + key offset; future keys and keys past the end
-          // both have key offset > lim
-          const int kq = j0 + 4 * h - (q0w + 32 * rb + c32);
-          const int lim = CAUSAL ? min(-kq, nk - 1) : nk - 1;
-#pragma unroll
-          for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
-              if (koff > lim) sacc[rb][kb][r] = -INFINITY;
-            }
-        }
-      }
-
-      // Row maxima; rows whose maximum moved past the slack are rescaled.
-      float muse[RB];
+      float rs[RB];
+      bool over = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][kb][r]);
-        mx = max_halves(mx) * c;
-        const bool need = mx > m[rb] + kRescaleSlack;
-        if (wave_any(need)) {
-          keep_branch();
-          const float mnew = need ? mx : m[rb];
-          const float alpha = !need ? 1.f : (m[rb] == -INFINITY) ? 0.f : fast_exp2(m[rb] - mnew);
-          m[rb] = mnew;
-          l[rb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
-        }
-        muse[rb] = (m[rb] == -INFINITY) ? 0.f : m[rb];
+        rs[rb] = exponentiate(sacc[rb], m[rb]);
+        over |= !(rs[rb] <= kMaxWeight);
       }
+      if (wave_any(over)) {
+        // Some row overflowed the bound: rows whose own share (either half)
+        // did so take the block's maximum, rescale O and l, and are
+        // exponentiated again; the other rows recompute the same values.
+        keep_branch();
+        f32x16 s2[RB][C::KB];
+        scores(Ks, j0, s2);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const bool own = !(rs[rb] <= kMaxWeight);
+          const bool row = max_halves(own ? 1.f : 0.f) > 0.f;
+          const float mx = block_max(s2[rb]);
+          if (row) {
+            const float alpha = fast_exp2(m[rb] - mx);
+            m[rb] = mx;
+            l[rb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+          }
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb) sacc[rb][kb] = s2[rb][kb];
+          rs[rb] = exponentiate(sacc[rb], m[rb]);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) l[rb] += rs[rb];
 
       // P^T as B operand (k-step u: registers 8*(u&1).. of key block u>>1,
-      // i.e. keys 16u + 8*(e>>2) + 4h + (e&3)), then O^T += V^T P^T with
-      // each V fragment feeding the RB row blocks.
+      // i.e. keys 16u + 8*(e>>2) + 4h + (e&3)), rounded to bf16, then
+      // O^T += V^T P^T with each V fragment feeding the RB row blocks.
 #pragma unroll
       for (int u = 0; u < C::PU; ++u) {
         bf16x8 pf[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          uint32_t pw[4];
-          float rs = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = fast_exp2(fmaf(sacc[rb][u >> 1][8 * (u & 1) + e], c, -muse[rb]));
-            const float p1 = fast_exp2(fmaf(sacc[rb][u >> 1][8 * (u & 1) + e + 1], c, -muse[rb]));
-            pw[e >> 1] = pack_bf16x2(p0, p1);
-            rs += p0 + p1;
-          }
-          l[rb] += rs;
-          pf[rb] = bf16x8_from(pw[0], pw[1], pw[2], pw[3]);
+          const f32x16& pv = sacc[rb][u >> 1];
+          const int r0 = 8 * (u & 1);
+          pf[rb] = bf16x8_from(pack_bf16x2(pv[r0], pv[r0 + 1]), pack_bf16x2(pv[r0 + 2], pv[r0 + 3]),
+                               pack_bf16x2(pv[r0 + 4], pv[r0 + 5]), pack_bf16x2(pv[r0 + 6], pv[r0 + 7]));
         }
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
@@ -280,8 +323,8 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int query = q0w + 32 * rb + c32;
-    const float lt = sum_halves(l[rb]);
-    const float inv = 1.f / lt;
+    const float lt = sum_halves(l[rb]);  // >= 1: the row maximum has weight >= 1
+    const float inv = __builtin_amdgcn_rcpf(lt);
     if constexpr (C::QL) {
       // O fragment (dims db*32 + 8g + 4h + 0..3 of this lane's row) into
       // this wavefront's rows of the Q staging tile
@@ -305,7 +348,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
           *reinterpret_cast<uint2*>(Or + db * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
         }
     }
-    if (h == 0 && query < N) LSE[(size_t)bh * N + query] = fmaf(m[rb], kLn2, logf(lt));
+    if (h == 0 && query < N) LSE[(size_t)bh * N + query] = (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2;
   }
   if constexpr (C::QL) {
     // rows back out of LDS as whole 16-byte chunks: 8 lanes per row, so each
