@@ -28,6 +28,7 @@ __all__ = [
     "scores",
     "softmax_rows",
     "attention_forward",
+    "attention_forward_keys",
     "attention_backward",
     "attention_forward_backward",
     "per_head",
@@ -84,6 +85,29 @@ def attention_forward(q, k, v, scale: float, causal: bool = False):
     p, m, l = softmax_rows(s)
     o = p @ v
     lse = m + torch.log(l)
+    return o, lse
+
+
+def attention_forward_keys(q, k, v, scale: float, causal: bool, lo: int, hi: int):
+    """O and LSE of every row over the keys lo <= j < hi only, in fp64.
+
+    One part of a row as the Flash-Decoding split produces it (CS324 Lecture
+    8, section 8.2): the three steps of standard attention with the keys
+    outside the part masked like future keys.  A row that sees no key of
+    the part has nothing to normalise: O = 0 and LSE = -inf (the identity of
+    the merge, exercise 3).
+    """
+    v = _as64(v)
+    s = scores(q, k, scale, causal)
+    kidx = torch.arange(s.shape[-1])
+    s = s.masked_fill((kidx < lo) | (kidx >= hi), float("-inf"))
+    m = s.max(dim=-1).values
+    empty = m == float("-inf")
+    e = torch.exp(s - torch.where(empty, torch.zeros_like(m), m).unsqueeze(-1))
+    l = e.sum(dim=-1)
+    p = e / torch.where(empty, torch.ones_like(l), l).unsqueeze(-1)
+    o = p @ v
+    lse = torch.where(empty, torch.full_like(m, float("-inf")), m + torch.log(l))
     return o, lse
 
 

@@ -29,6 +29,7 @@ __all__ = [
     "blocks",
     "merge",
     "merge_with_output",
+    "merge_parts",
     "softmax_from_stats",
 ]
 
@@ -95,3 +96,35 @@ def merge_with_output(m1, l1, o1, m2, l2, o2):
 def softmax_from_stats(xs: Sequence[float], m: float, l: float) -> List[float]:
     """softmax(x)_j = exp(x_j - m) / l once the whole row has been read."""
     return [math.exp(x - m) / l for x in xs]
+
+
+def merge_parts(lse_parts, o_parts):
+    """Merge S partial results of the same rows, part by part (fp64 torch).
+
+    lse_parts: [S, ...] natural-log log-sum-exps of each part (-inf for a
+    part with no key); o_parts: [S, ..., d] each part's output normalised
+    over its own keys.  A part's running state is (m, l) = (L_s, 1), since
+    e^{L_s} = l_s e^{m_s}; the parts are folded one after another with the
+    update of ``merge`` (exercise 3) and the output is un-normalised, moved
+    to the common base and re-normalised as in ``merge_with_output``
+    (exercise 7, section 8.2).  Returns (LSE, O); a row whose parts are all
+    empty gets LSE = -inf and O = 0.
+    """
+    import torch
+
+    ninf = float("-inf")
+    m = lse_parts[0].clone()
+    l = torch.where(m == ninf, torch.zeros_like(m), torch.ones_like(m))
+    o = o_parts[0].clone()
+    for s in range(1, lse_parts.shape[0]):
+        ms = lse_parts[s]
+        mn = torch.maximum(m, ms)
+        safe = torch.where(mn == ninf, torch.zeros_like(mn), mn)
+        a = torch.where(m == ninf, torch.zeros_like(m), l * torch.exp(m - safe))
+        b = torch.where(ms == ninf, torch.zeros_like(ms), torch.exp(ms - safe))
+        ln = a + b
+        den = torch.where(ln > 0, ln, torch.ones_like(ln))
+        o = (a.unsqueeze(-1) * o + b.unsqueeze(-1) * o_parts[s]) / den.unsqueeze(-1)
+        m, l = mn, ln
+    lse = torch.where(l > 0, m + torch.log(torch.where(l > 0, l, torch.ones_like(l))), torch.full_like(m, ninf))
+    return lse, o

@@ -297,3 +297,58 @@ def test_causal_block_skipping_counts_page_example():
     T.forward_outer_kv(q, k, v, 0.2, True, n // nblk, n // nblk, io)
     assert io.pairs == needed
     assert round(needed / nblk**2, 3) == float(rows[3])
+
+
+# --------------------------------------------------------------------------
+# split-KV parts and their merge (CS324 Lecture 8, section 8.2, exercises 3, 7)
+
+def test_merge_parts_matches_page_exercise_in_lse_form():
+    # each part's (m, l) becomes the single number LSE = m + ln l; the merged
+    # LSE must be the exercise's merged state in the same form
+    rows = {r[0]: r[1:] for r in read_golden("online_softmax_merge.txt")}
+    lse = [float(rows[k][0]) + math.log(float(rows[k][1])) for k in ("state1", "state2")]
+    want = float(rows["merged"][0]) + math.log(float(rows["merged"][1]))
+    got, o = OS.merge_parts(torch.tensor(lse, dtype=F64).reshape(2, 1),
+                            torch.zeros((2, 1, 3), dtype=F64))
+    assert got.item() == pytest.approx(want, abs=1e-6)
+    assert float(o.abs().max()) == 0.0
+
+
+def test_merge_parts_equals_pairwise_scalar_merge():
+    # folding the vectorised merge over parts = folding the scalar
+    # merge_with_output (itself pinned above), with empty parts mixed in
+    S, R, d = 4, 9, 3
+    lse = rnd((S, R), 31) * 3
+    lse[1, 2] = -math.inf
+    lse[:, 5] = -math.inf                # a row with no key in any part
+    lse[2, 7] = -math.inf
+    o = rnd((S, R, d), 32)
+    got_lse, got_o = OS.merge_parts(lse, o)
+    for r in range(R):
+        m, l, acc = lse[0, r].item(), (0.0 if lse[0, r].item() == -math.inf else 1.0), o[0, r].tolist()
+        for s in range(1, S):
+            ls = lse[s, r].item()
+            m, l, acc = OS.merge_with_output(m, l, acc, ls, 0.0 if ls == -math.inf else 1.0, o[s, r].tolist()) \
+                if (m != -math.inf or ls != -math.inf) else (m, 0.0, [0.0] * d)
+        if l == 0.0:
+            assert got_lse[r].item() == -math.inf and float(got_o[r].abs().max()) == 0.0
+        else:
+            assert got_lse[r].item() == pytest.approx(m + math.log(l), abs=1e-14)
+            assert max(abs(a - b) for a, b in zip(got_o[r].tolist(), acc)) <= 1e-14
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_parts_merged_equal_whole_row_attention(causal):
+    # blockwise = whole-row (CS324 Lecture 8, section 5.2 demo; section 8.2):
+    # attention over disjoint key ranges, merged, is attention over all keys
+    n, d, scale = 70, 8, 0.3
+    q, k, v = rnd((n, d), 41), rnd((n, d), 42), rnd((n, d), 43)
+    o_ref, lse_ref = A.attention_forward(q, k, v, scale, causal)
+    cuts = [0, 17, 40, 64, 70, 70]      # uneven ranges and an empty last range
+    parts = [A.attention_forward_keys(q, k, v, scale, causal, lo, hi) for lo, hi in zip(cuts, cuts[1:])]
+    lse, o = OS.merge_parts(torch.stack([p[1] for p in parts]), torch.stack([p[0] for p in parts]))
+    assert torch.allclose(lse, lse_ref, atol=1e-13, rtol=0)
+    assert torch.allclose(o, o_ref, atol=1e-13, rtol=0)
+    if causal:
+        # row 3 sees no key of the range [17, 40): O = 0, LSE = -inf there
+        assert parts[1][1][3].item() == -math.inf and float(parts[1][0][3].abs().max()) == 0.0
