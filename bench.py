@@ -45,6 +45,9 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2_medium")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward kernel")
+    ap.add_argument("--splits", type=int, default=1,
+                    help="forward through fa_forward_split with this many key ranges "
+                         "(implies --fwd-only when > 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -87,7 +90,7 @@ def algorithmic(w, kernel, elem_bytes):
     """
     e = elem_bytes
     pairs = visible_pairs(w)
-    if kernel == "fwd":
+    if kernel in ("fwd", "fwd_split"):  # fwd_split: partial kernel + merge, timed together
         return "mfma", 2 * 2 * w.d * pairs, "FLOP"
     if kernel == "bwd_dkdv":
         return "mfma", 4 * 2 * w.d * pairs, "FLOP"
@@ -177,6 +180,8 @@ def main(argv=None):
     from exact_io_aware_09_amd.workloads import WORKLOADS, workload_inputs
 
     w = WORKLOADS[args.workload]
+    if args.splits > 1:
+        args.fwd_only = True
     dtype_name = "bf16" if w.dtype == torch.bfloat16 else "f32"
     dt = _lib.FA_BF16 if dtype_name == "bf16" else _lib.FA_F32
     dev = torch.device("cuda:0")
@@ -187,6 +192,8 @@ def main(argv=None):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     wsb = fa.workspace_bytes(B, H, N, d, w.dtype)
+    if args.splits > 1:
+        wsb = max(wsb, _lib.fa_forward_split_workspace_bytes(B, H, N, d, args.splits, dt))
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -200,8 +207,13 @@ def main(argv=None):
         """One step; if `ev` is given, record events between the kernels."""
         rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
         rec(0)
-        call(_lib.fa_forward(P[0], P[1], P[2], P[3], P[4], B, H, N, d, w.scale, int(w.causal),
-                             dt, sp), "fa_forward")
+        if args.splits > 1:
+            call(_lib.fa_forward_split(P[0], P[1], P[2], P[3], P[4], P[9], wsb, B, H, N, d,
+                                       w.scale, int(w.causal), args.splits, dt, sp),
+                 "fa_forward_split")
+        else:
+            call(_lib.fa_forward(P[0], P[1], P[2], P[3], P[4], B, H, N, d, w.scale,
+                                 int(w.causal), dt, sp), "fa_forward")
         rec(1)
         if args.fwd_only:
             return
@@ -230,7 +242,7 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    names = KERNELS[: nev - 1]
+    names = ("fwd_split",) if args.splits > 1 else KERNELS[: nev - 1]
     per_kernel = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                   for i, n in enumerate(names)}
 
@@ -247,7 +259,8 @@ def main(argv=None):
 
     result = {
         "metric": METRIC if (args.workload == "gpt2_medium" and not args.fwd_only)
-        else f"attention {'fwd' if args.fwd_only else 'fwd+bwd'} TFLOP/s ({args.workload})",
+        else (f"attention {'fwd' if args.fwd_only else 'fwd+bwd'} TFLOP/s ({args.workload}"
+              + (f", {args.splits} key ranges)" if args.splits > 1 else ")")),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -261,7 +274,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                    "scale": w.scale, "input_dtype": dtype_name,
-                   "step": "forward" if args.fwd_only else "forward+backward"},
+                   "step": "forward" if args.fwd_only else "forward+backward",
+                   **({"splits": args.splits} if args.splits > 1 else {})},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),

@@ -32,6 +32,9 @@ SIGNATURES = {
     "fa_version": (_I, []),
     "fa_strerror": (ctypes.c_char_p, [_I]),
     "fa_forward": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _F, _I, _I, _VP]),
+    "fa_forward_split_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "fa_forward_split": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I, _I, _I, _I, _F, _I, _I, _I, _VP]),
+    "fa_merge_partials": (_I, [_VP, _VP, _I, _VP, _VP, _I, _I, _I, _I, _I, _VP]),
     "fa_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_backward": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                          _I, _I, _I, _I, _F, _I, _I, _VP]),
@@ -85,6 +88,23 @@ def fa_forward(Q, K, V, O, LSE, B, H, N, d, scale, causal, dtype, stream) -> int
     """Raw call: device pointers as ints, returns the C return code."""
     return int(load().fa_forward(Q, K, V, O, LSE, B, H, N, d, float(scale), int(causal),
                                  int(dtype), stream))
+
+
+def fa_forward_split_workspace_bytes(B, H, N, d, splits, dtype) -> int:
+    return int(load().fa_forward_split_workspace_bytes(B, H, N, d, int(splits), int(dtype)))
+
+
+def fa_forward_split(Q, K, V, O, LSE, workspace, workspace_bytes, B, H, N, d, scale, causal,
+                     splits, dtype, stream) -> int:
+    """Raw call: device pointers as ints, returns the C return code."""
+    return int(load().fa_forward_split(Q, K, V, O, LSE, workspace, workspace_bytes, B, H, N, d,
+                                       float(scale), int(causal), int(splits), int(dtype), stream))
+
+
+def fa_merge_partials(O_parts, LSE_parts, splits, O, LSE, B, H, N, d, dtype, stream) -> int:
+    """Raw call: device pointers as ints, returns the C return code."""
+    return int(load().fa_merge_partials(O_parts, LSE_parts, int(splits), O, LSE, B, H, N, d,
+                                        int(dtype), stream))
 
 
 def fa_backward_workspace_bytes(B, H, N, d, dtype) -> int:

@@ -54,6 +54,42 @@ def forward(q, k, v, scale: float, causal: bool = False, out=None, lse=None):
     return o, lse_t
 
 
+def forward_split(q, k, v, scale: float, causal: bool = False, splits: int = 2, workspace=None,
+                  out=None, lse=None):
+    """``forward`` through the split-KV entry point (bfloat16 for splits > 1)."""
+    _check("q", q)
+    _check("k", k, q)
+    _check("v", v, q)
+    B, H, N, d, dt = _dims(q)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check("out", o, q)
+    need = _lib.fa_forward_split_workspace_bytes(B, H, N, d, splits, dt)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    rc = _lib.fa_forward_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse_t.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                               B, H, N, d, scale, int(bool(causal)), splits, dt, _stream(q.device))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_forward_split")
+    return o, lse_t
+
+
+def merge_partials(o_parts, lse_parts, dtype=torch.bfloat16):
+    """Merge float32 partial results [S, B, H, N, d] / [S, B, H, N] into (O, LSE)."""
+    if o_parts.dim() != 5 or o_parts.dtype != torch.float32 or not o_parts.is_contiguous():
+        raise ValueError("o_parts must be contiguous float32 [S, B, H, N, d]")
+    S, B, H, N, d = o_parts.shape
+    if lse_parts.shape != (S, B, H, N) or lse_parts.dtype != torch.float32 or not lse_parts.is_contiguous():
+        raise ValueError("lse_parts must be contiguous float32 [S, B, H, N]")
+    o = torch.empty((B, H, N, d), dtype=dtype, device=o_parts.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    rc = _lib.fa_merge_partials(o_parts.data_ptr(), lse_parts.data_ptr(), S, o.data_ptr(),
+                                lse.data_ptr(), B, H, N, d, _DTYPES[dtype], _stream(o_parts.device))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_merge_partials")
+    return o, lse
+
+
 def workspace_bytes(B, H, N, d, dtype) -> int:
     return _lib.fa_backward_workspace_bytes(B, H, N, d, _DTYPES[dtype])
 

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -34,6 +34,14 @@ int check_common(int B, int H, int N, int d, float scale, int causal, int dtype)
   return FA_OK;
 }
 
+constexpr int kMaxSplits = 256;
+
+// Split-forward workspace: the partial outputs [splits, rows, d], then the
+// partial log-sum-exps [splits, rows] from a 256-byte aligned offset.
+size_t split_lse_offset(size_t rows, int d, int splits) {
+  return ((size_t)splits * rows * d * sizeof(float) + 255) & ~(size_t)255;
+}
+
 }  // namespace
 
 extern "C" {
@@ -46,7 +54,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size, scale not finite and > 0, causal not 0/1)";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration (d must be 64, 128 or 256; dtype FA_BF16 or FA_F32; sizes below 2^31)";
     case FA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
-    case FA_ERR_NO_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_bytes()";
+    case FA_ERR_NO_WORKSPACE: return "workspace missing or smaller than the *_workspace_bytes() size";
     case FA_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown error code";
   }
@@ -65,6 +73,51 @@ int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
                      ? fa::launch_forward_bf16(Q, K, V, O, LSE, p, s)
                      : fa::launch_forward_f32((const float*)Q, (const float*)K, (const float*)V,
                                               (float*)O, LSE, p, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_forward_split_workspace_bytes(int B, int H, int N, int d, int splits, int dtype) {
+  if (check_sizes(B, H, N, d, dtype) != FA_OK || splits < 1 || splits > kMaxSplits) return 0;
+  if (splits == 1) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return split_lse_offset(rows, d, splits) + (size_t)splits * rows * sizeof(float);
+}
+
+int fa_forward_split(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                     float scale, int causal, int splits, int dtype, void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (splits < 1 || splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  if (splits == 1) return fa_forward(Q, K, V, O, LSE, B, H, N, d, scale, causal, dtype, stream);
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_forward_split_workspace_bytes(B, H, N, d, splits, dtype))
+    return FA_ERR_NO_WORKSPACE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE) ||
+      !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t rows = (size_t)B * H * N;
+  float* Opart = static_cast<float*>(workspace);
+  float* Lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_lse_offset(rows, d, splits));
+  hipError_t e = fa::launch_forward_split_bf16(Q, K, V, p, splits, Opart, Lpart, s);
+  if (e == hipSuccess) e = fa::launch_merge(Opart, Lpart, splits, O, LSE, p, true, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_merge_partials(const float* O_parts, const float* LSE_parts, int splits, void* O, float* LSE,
+                      int B, int H, int N, int d, int dtype, void* stream) {
+  int rc = check_sizes(B, H, N, d, dtype);
+  if (rc != FA_OK) return rc;
+  if (splits < 1 || splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  if (!O_parts || !LSE_parts || !O || !LSE) return FA_ERR_INVALID_ARG;
+  if (!aligned16(O_parts) || !aligned16(LSE_parts) || !aligned16(O) || !aligned16(LSE))
+    return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, 1.0f, false};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = fa::launch_merge(O_parts, LSE_parts, splits, O, LSE, p, dtype == FA_BF16, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -71,11 +71,18 @@ struct FwdCfg {
 // A wavefront owns RB blocks of 32 query rows: every K and V fragment read
 // from LDS feeds RB matrix instructions, which divides LDS reads and
 // HBM->LDS copies per FLOP by RB.
-template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL>
+//
+// SPLIT: the keys are cut into ranges of sa.span keys (a multiple of 64);
+// workgroup (tile, range) runs the loop over its range only and writes the
+// range's partial result -- O normalised over the range (float32) and the
+// range's log-sum-exp, -inf for rows that see no key of the range -- to
+// sa.Opart / sa.Lpart, for merge_kernel to combine.
+template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64, OCC)
 void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      const bf16_t* __restrict__ V, bf16_t* __restrict__ O,
-                     float* __restrict__ LSE, int BH, int N, int nqb, int G, float c) {
+                     float* __restrict__ LSE, int BH, int N, int nqb, int G, float c,
+                     SplitArgs sa = {}) {
   using C = FwdCfg<D, NW, RB, BC, ST>;
   // One LDS variable per stage and operand: with the stage a compile-time
   // constant at every access, the compiler can tell the block being read
@@ -96,8 +103,15 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   };
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
-  int bh, rank;
-  grouped_order(xcd_remap(blockIdx.x, BH * nqb), nqb, BH, G, bh, rank);
+  int bh, rank, split = 0;
+  if constexpr (SPLIT) {
+    // the ranges of one tile are adjacent in the order
+    const int L = xcd_remap(blockIdx.x, BH * nqb * sa.splits);
+    split = L % sa.splits;
+    grouped_order(L / sa.splits, nqb, BH, G, bh, rank);
+  } else {
+    grouped_order(xcd_remap(blockIdx.x, BH * nqb), nqb, BH, G, bh, rank);
+  }
   const int qb = CAUSAL ? (nqb - 1 - rank) : rank;  // longest causal blocks first
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
@@ -108,12 +122,33 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   const int q0w = q0 + w * C::RW;  // first query row of this wavefront
   // this lane's query row in row block rb is q0w + 32 * rb + c32
 
-  const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
-  const int ntiles = (kend + BC - 1) / BC;
+  // keys [kbase, kend) of this workgroup: blocks kbase + t*BC, t < ntiles
+  const int kbase = SPLIT ? split * sa.span : 0;
+  const int kend0 = CAUSAL ? min(N, q0 + C::BR) : N;
+  const int kend = SPLIT ? min(kend0, kbase + sa.span) : kend0;
+  const int ntiles = kend > kbase ? (kend - kbase + BC - 1) / BC : 0;
+  if constexpr (SPLIT) {
+    if (ntiles == 0) {
+      // no key of the range is visible to any row of the tile
+      const size_t rows = (size_t)BH * N;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int query = q0w + 32 * rb + c32;
+        if (query < N) {
+          if (h == 0) sa.Lpart[split * rows + (size_t)bh * N + query] = -INFINITY;
+          float* Op = sa.Opart + (split * rows + (size_t)bh * N + query) * D;
+#pragma unroll
+          for (int cc = 0; cc < D / 2; cc += 4)
+            *reinterpret_cast<float4*>(Op + h * (D / 2) + cc) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+      return;
+    }
+  }
 
   auto fetch = [&](int t, auto S) {
-    dma_tile<D, BC, C::NT>(rk, t * BC, kst(S), tid);
-    dma_tile<D, BC, C::NT>(rv, t * BC, vst(S), tid);
+    dma_tile<D, BC, C::NT>(rk, kbase + t * BC, kst(S), tid);
+    dma_tile<D, BC, C::NT>(rv, kbase + t * BC, vst(S), tid);
   };
   // The first K/V copies go out before Q is read, so that the latencies
   // overlap.
@@ -154,6 +189,10 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 
   f32x16 oacc[RB][C::DB];
   float m[RB], l[RB];
+  // Base of the exponent.  Every row sees key 0 of its first block, so m is
+  // finite -- except for a key range that starts after a causal row, which
+  // sees nothing of the range: its weights are then exp2(-inf) = 0.
+  auto base = [](float mrow) { return (SPLIT && CAUSAL && mrow == -INFINITY) ? 0.f : mrow; };
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -232,7 +271,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
     // the stage of step t-1 is free (barrier at the end of the last step)
     if (t + ST - 1 < ntiles) fetch(t + ST - 1, std::integral_constant<int, SN>{});
-    const int j0 = t * BC;
+    const int j0 = kbase + t * BC;
     const bool active = !CAUSAL || j0 <= q0w + C::RW - 1;
     if (active) {
       const bf16_t* Ks = kst(S);
@@ -252,7 +291,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
       bool over = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        rs[rb] = exponentiate(sacc[rb], m[rb]);
+        rs[rb] = exponentiate(sacc[rb], base(m[rb]));
         over |= !(rs[rb] <= kMaxWeight);
       }
       if (wave_any(over)) {
@@ -278,7 +317,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
           }
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb) sacc[rb][kb] = s2[rb][kb];
-          rs[rb] = exponentiate(sacc[rb], m[rb]);
+          rs[rb] = exponentiate(sacc[rb], base(m[rb]));
         }
       }
 #pragma unroll
@@ -317,6 +356,32 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     if constexpr (ST > 2) {
       if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>{});
     }
+  }
+
+  if constexpr (SPLIT) {
+    // Partial result of the range: O normalised over it (float32, each lane
+    // its 4-value groups db*32 + 8g + 4h + 0..3) and its log-sum-exp; a row
+    // that saw no key of the range has l = 0 and gets O = 0, LSE = -inf.
+    const size_t rows = (size_t)BH * N;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int query = q0w + 32 * rb + c32;
+      const float lt = sum_halves(l[rb]);
+      const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
+      if (query < N) {
+        const size_t r = split * rows + (size_t)bh * N + query;
+        float* Op = sa.Opart + r * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(Op + db * 32 + 8 * g + 4 * h) =
+                make_float4(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv,
+                            oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
+        if (h == 0) sa.Lpart[r] = lt > 0.f ? (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+      }
+    }
+    return;
   }
 
   // Epilogue: O = acc / l (bf16), LSE = m ln2 + ln l (fp32, natural log).
@@ -387,6 +452,96 @@ hipError_t run_fwd_c(const void* Q, const void* K, const void* V, void* O, float
                   : run_fwd<D, NW, RB, BC, ST, OCC, false>(Q, K, V, O, LSE, p, stream);
 }
 
+// Merge of partial results (CS324 notes, exercises 3 and 7, and the
+// Flash-Decoding scheme of section 8.2): for each row, with L_s the parts'
+// log-sum-exps and M = max_s L_s,
+//   LSE = M + ln sum_s e^{L_s - M},   O = sum_s e^{L_s - LSE} O_s,
+// which is the pairwise merge of (m, l, O) states applied to all parts at
+// once (a part's state is (L_s, 1) up to the common factor).  Parts with
+// L_s = -inf carry no weight and their O_s is not read.  D/4 lanes per row,
+// four consecutive values each; memory-bound.
+template <int D, typename OutT>
+__global__ __launch_bounds__(256)
+void merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpart, int splits,
+                  long long rows, OutT* __restrict__ O, float* __restrict__ LSE) {
+  constexpr int TPR = D / 4;       // lanes per row
+  constexpr int RPB = 256 / TPR;   // rows per workgroup
+  const int tid = threadIdx.x;
+  const long long row = (long long)blockIdx.x * RPB + tid / TPR;
+  const int part = tid % TPR;
+  if (row >= rows) return;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, Lpart[s * rows + row]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float sum = 0.f;
+  if (M > -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float Ls = Lpart[s * rows + row];
+      if (Ls == -INFINITY) continue;
+      const float wgt = expf(Ls - M);
+      const float4 v = *reinterpret_cast<const float4*>(Opart + ((size_t)s * rows + row) * D + 4 * part);
+      sum += wgt;
+      acc.x = fmaf(wgt, v.x, acc.x);
+      acc.y = fmaf(wgt, v.y, acc.y);
+      acc.z = fmaf(wgt, v.z, acc.z);
+      acc.w = fmaf(wgt, v.w, acc.w);
+    }
+  }
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if constexpr (sizeof(OutT) == 2) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(O) + row * D + 4 * part) =
+        make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(O) + row * D + 4 * part) = o;
+  }
+  if (part == 0) LSE[row] = sum > 0.f ? M + logf(sum) : -INFINITY;
+}
+
+template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL>
+hipError_t run_fwd_split(const void* Q, const void* K, const void* V, const Problem& p,
+                         int splits, float* Opart, float* Lpart, hipStream_t stream) {
+  using C = FwdCfg<D, NW, RB, BC, ST>;
+  const int BH = p.B * p.H;
+  const int nqb = (p.N + C::BR - 1) / C::BR;
+  const long long grid = (long long)BH * nqb * splits;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const float c = p.scale * kLog2e;
+  const int G = head_group(OCC * 4 / NW, nqb);
+  SplitArgs sa;
+  sa.span = split_span(p.N, splits);
+  sa.splits = splits;
+  sa.Opart = Opart;
+  sa.Lpart = Lpart;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, true>), dim3((unsigned)grid),
+                     dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                     (bf16_t*)nullptr, (float*)nullptr, BH, p.N, nqb, G, c, sa);
+  return hipGetLastError();
+}
+
+template <int D, int NW, int RB, int BC, int ST, int OCC>
+hipError_t run_fwd_split_c(const void* Q, const void* K, const void* V, const Problem& p,
+                           int splits, float* Opart, float* Lpart, hipStream_t stream) {
+  return p.causal
+             ? run_fwd_split<D, NW, RB, BC, ST, OCC, true>(Q, K, V, p, splits, Opart, Lpart, stream)
+             : run_fwd_split<D, NW, RB, BC, ST, OCC, false>(Q, K, V, p, splits, Opart, Lpart, stream);
+}
+
+template <int D>
+hipError_t run_merge(const float* Opart, const float* Lpart, int splits, void* O, float* LSE,
+                     long long rows, bool bf16, hipStream_t stream) {
+  constexpr int RPB = 256 / (D / 4);
+  const long long grid = (rows + RPB - 1) / RPB;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (bf16)
+    hipLaunchKernelGGL((merge_kernel<D, bf16_t>), dim3((unsigned)grid), dim3(256), 0, stream, Opart,
+                       Lpart, splits, rows, (bf16_t*)O, LSE);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, float>), dim3((unsigned)grid), dim3(256), 0, stream, Opart,
+                       Lpart, splits, rows, (float*)O, LSE);
+  return hipGetLastError();
+}
+
 // Launch configurations per head dim: wavefronts per workgroup, 32-row
 // query blocks per wavefront, keys per K/V block, pipeline stages, minimum
 // wavefronts per SIMD.
@@ -401,6 +556,27 @@ hipError_t run_fwd_c(const void* Q, const void* K, const void* V, void* O, float
 #endif
 
 }  // namespace
+
+hipError_t launch_forward_split_bf16(const void* Q, const void* K, const void* V, const Problem& p,
+                                     int splits, float* Opart, float* Lpart, hipStream_t stream) {
+  switch (p.d) {
+    case 64: return run_fwd_split_c<64, FA_FWD_CFG_D64>(Q, K, V, p, splits, Opart, Lpart, stream);
+    case 128: return run_fwd_split_c<128, FA_FWD_CFG_D128>(Q, K, V, p, splits, Opart, Lpart, stream);
+    case 256: return run_fwd_split_c<256, FA_FWD_CFG_D256>(Q, K, V, p, splits, Opart, Lpart, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_merge(const float* Opart, const float* Lpart, int splits, void* O, float* LSE,
+                        const Problem& p, bool bf16, hipStream_t stream) {
+  const long long rows = (long long)p.B * p.H * p.N;
+  switch (p.d) {
+    case 64: return run_merge<64>(Opart, Lpart, splits, O, LSE, rows, bf16, stream);
+    case 128: return run_merge<128>(Opart, Lpart, splits, O, LSE, rows, bf16, stream);
+    case 256: return run_merge<256>(Opart, Lpart, splits, O, LSE, rows, bf16, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_forward_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                const Problem& p, hipStream_t stream) {

@@ -10,9 +10,30 @@ struct Problem {
   bool causal;
 };
 
+// Key ranges of the split forward: `span` keys each (a multiple of 64, so
+// of every K/V block size), the last ranges possibly short or empty.
+inline int split_span(int N, int splits) {
+  const int per = (N + splits - 1) / splits;
+  return (per + 63) / 64 * 64;
+}
+
+struct SplitArgs {
+  int span = 0, splits = 1;
+  float* Opart = nullptr;  // [splits, B*H*N, d] float32
+  float* Lpart = nullptr;  // [splits, B*H*N] float32
+};
+
 // bfloat16 inputs, fp32 accumulation on the matrix cores.
 hipError_t launch_forward_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                const Problem& p, hipStream_t stream);
+// Split forward: partial results of every key range into Opart / Lpart;
+// then the merge of `splits` partial results into O (bf16 or float32) and
+// LSE.
+hipError_t launch_forward_split_bf16(const void* Q, const void* K, const void* V, const Problem& p,
+                                     int splits, float* Opart, float* Lpart, hipStream_t stream);
+hipError_t launch_merge(const float* Opart, const float* Lpart, int splits, void* O, float* LSE,
+                        const Problem& p, bool bf16, hipStream_t stream);
+
 // Backward workspace: -D (one float per query row), then, starting at float
 // index ws_lse_offset(rows), LSE * log2(e) (one float per row).
 inline long long ws_lse_offset(long long rows) { return (rows + 63) & ~63LL; }

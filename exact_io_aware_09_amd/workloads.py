@@ -13,8 +13,10 @@ memory-footprint shape (B 16, H 8, N 4096, d 64) measured on A100 in
 "FlashAttention and GPU memory" sections 01, 09 and 10; the N = 65,536
 long-sequence shape from the same section; and head dim 256 at long
 sequence, where the third version's forward throughput is quoted (section
-11).  Synthetic N(0, 1) data stands in for activations because the pages time
-the operation itself, not a trained model.
+11); and a small-batch, few-head shape (B 1, H 8, N 4096, d 64) whose 256
+query blocks alone leave most of the GPU idle, the case of the key-split forward
+("Lecture 8", section 8.2).  Synthetic N(0, 1) data stands in for activations
+because the pages time the operation itself, not a trained model.
 """
 from __future__ import annotations
 
@@ -55,6 +57,10 @@ WORKLOADS = {
                      description="long sequence, bf16, causal, no N x N buffer"),
     "big_d": Workload("big_d", 2, 16, 16384, 256, torch.bfloat16, False, 1.0 / 16.0, 4, mult=0.5,
                       sampled=True, description="head dim 256, bf16 x0.5, non-causal"),
+    # the split-KV forward's case: B*H*N/128 = 256 query blocks, one per CU,
+    # a quarter of the workgroups the GPU holds at once
+    "few_heads": Workload("few_heads", 1, 8, 4096, 64, torch.bfloat16, False, 1.0 / 8.0, 5,
+                          sampled=True, description="small batch, few heads, bf16, non-causal"),
 }
 
 

@@ -78,6 +78,51 @@ int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
                void* stream);
 
 /*
+ * Split-KV forward (the Flash-Decoding scheme of CS324 notes section 8.2):
+ * the keys of every row are cut into `splits` contiguous ranges of
+ * span = 64 * ceil(ceil(N / splits) / 64) keys (the last ranges may be
+ * shorter or empty).  One workgroup per (head, query block, range) runs the
+ * forward's tile loop over its range only, so that B*H*N/128 * splits
+ * workgroups share the GPU when B*H*N/128 alone would leave it idle
+ * (small batch, few heads).  Each writes a partial result -- the range's O,
+ * normalised over the range (float32), and the range's log-sum-exp (-inf for
+ * a row that sees no key of the range) -- to `workspace`, and a second
+ * kernel merges the ranges of every row with the online-softmax merge
+ * (exercises 3 and 7 of those notes; see fa_merge_partials).  O and LSE mean
+ * exactly what fa_forward writes; the result differs from fa_forward's only
+ * by rounding (the ranges are summed in float32 before O is rounded).
+ *
+ * splits: 1..256.  splits == 1 is fa_forward itself (workspace unused, may
+ * be NULL; every dtype).  splits > 1 supports FA_BF16 only
+ * (FA_ERR_UNSUPPORTED otherwise) and needs `workspace` of at least
+ * fa_forward_split_workspace_bytes() bytes (contents ignored on entry):
+ * partial outputs float32 [splits, B*H*N, d], then from the next 256-byte
+ * boundary partial log-sum-exps float32 [splits, B*H*N].
+ * fa_forward_split_workspace_bytes returns 0 for splits == 1 and for
+ * invalid sizes.
+ */
+size_t fa_forward_split_workspace_bytes(int B, int H, int N, int d, int splits, int dtype);
+
+int fa_forward_split(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                     float scale, int causal, int splits, int dtype, void* stream);
+
+/*
+ * Merge of partial attention results over disjoint key sets (CS324 notes
+ * exercises 3 and 7, section 8.2).  O_parts: float32 [splits, B*H*N, d],
+ * part s's output for each row normalised over part s's keys; LSE_parts:
+ * float32 [splits, B*H*N], part s's natural-log log-sum-exp L_s, -inf when
+ * part s holds no key for the row (its O_parts row is then not read).  With
+ * M = max_s L_s, writes LSE = M + ln sum_s e^{L_s - M} and
+ * O = sum_s e^{L_s - LSE} O_s, rounded to `dtype` (FA_BF16 or FA_F32);
+ * a row whose parts are all empty gets O = 0, LSE = -inf.  This is the
+ * merge a sequence-parallel caller applies to the results of different
+ * devices.  splits: 1..256; d in {64, 128, 256}; pointers 16-byte aligned.
+ */
+int fa_merge_partials(const float* O_parts, const float* LSE_parts, int splits, void* O,
+                      float* LSE, int B, int H, int N, int d, int dtype, void* stream);
+
+/*
  * Bytes of device workspace fa_backward needs: two float32 vectors of one
  * value per query row (B*H*N rows), each starting on a 256-byte boundary --
  * -D_i = -sum_k dO_ik O_ik (D is the vector of CS324 notes section 5.4;

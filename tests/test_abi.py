@@ -99,3 +99,47 @@ def test_backward_validation(args, code):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load(tmp_path / "nope.so")
+
+
+def test_split_workspace_bytes():
+    rows = 2 * 3 * 100
+    # partial outputs [splits, rows, d] float32, then partial LSE [splits, rows] from 256-aligned
+    po = 4 * rows * 64 * 4
+    assert fa.fa_forward_split_workspace_bytes(2, 3, 100, 64, 4, 0) == ((po + 255) // 256) * 256 + 4 * rows * 4
+    assert fa.fa_forward_split_workspace_bytes(2, 3, 100, 64, 1, 0) == 0   # splits == 1: plain forward
+    assert fa.fa_forward_split_workspace_bytes(2, 3, 100, 64, 0, 0) == 0   # invalid
+    assert fa.fa_forward_split_workspace_bytes(2, 3, 100, 64, 257, 0) == 0
+    assert fa.fa_forward_split_workspace_bytes(2, 3, 100, 96, 2, 0) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(splits=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(splits=257), _lib.FA_ERR_INVALID_ARG),
+    (dict(dtype=_lib.FA_F32), _lib.FA_ERR_UNSUPPORTED),
+    (dict(workspace=0), _lib.FA_ERR_NO_WORKSPACE),
+    (dict(workspace_bytes=16), _lib.FA_ERR_NO_WORKSPACE),
+    (dict(O=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(workspace=A + 8), _lib.FA_ERR_MISALIGNED),
+    (dict(d=80), _lib.FA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), _lib.FA_ERR_INVALID_ARG),
+])
+def test_forward_split_validation(args, code):
+    kw = dict(Q=A, K=A, V=A, O=A, LSE=A, workspace=A, workspace_bytes=1 << 40, B=1, H=1, N=128,
+              d=64, scale=0.125, causal=0, splits=2, dtype=_lib.FA_BF16, stream=None)
+    kw.update(args)
+    assert fa.fa_forward_split(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(splits=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(O_parts=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(LSE_parts=A + 4), _lib.FA_ERR_MISALIGNED),
+    (dict(d=32), _lib.FA_ERR_UNSUPPORTED),
+    (dict(dtype=3), _lib.FA_ERR_UNSUPPORTED),
+    (dict(B=0), _lib.FA_ERR_INVALID_ARG),
+])
+def test_merge_partials_validation(args, code):
+    kw = dict(O_parts=A, LSE_parts=A, splits=3, O=A, LSE=A, B=1, H=2, N=64, d=64,
+              dtype=_lib.FA_BF16, stream=None)
+    kw.update(args)
+    assert fa.fa_merge_partials(**kw) == code

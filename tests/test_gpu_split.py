@@ -1,0 +1,148 @@
+"""GPU parity of the split-KV forward and of the merge of partial results.
+
+The split forward must give what fa_forward gives -- standard attention --
+within the bfloat16 tolerances (O <= 2e-2, LSE <= 1e-3 max-abs).  Its partial
+results in the workspace are checked against the oracle's attention over
+each key range, and fa_merge_partials against the oracle's fold of the
+exercise-3 merge.
+"""
+import math
+
+import pytest
+import torch
+
+import exact_io_aware_09_amd as fa
+from exact_io_aware_09_amd import _lib
+from exact_io_aware_09_amd.workloads import WORKLOADS, make_inputs, sample_rows, workload_inputs
+from oracle import attention as A
+from oracle import online_softmax as OS
+from oracle import sampled as SM
+
+pytestmark = pytest.mark.gpu
+
+O_TOL, LSE_TOL = 2e-2, 1e-3
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def max_abs(a, b):
+    return float((a.double() - b.double()).abs().max()) if a.numel() else 0.0
+
+
+def span_of(N, splits):
+    per = -(-N // splits)
+    return -(-per // 64) * 64
+
+
+def split_raw(q, k, v, scale, causal, splits):
+    """fa_forward_split through the C ABI; returns (O, LSE, partial O, partial LSE) on the CPU."""
+    B, H, N, d = q.shape
+    qd, kd, vd = (t.to(dev()) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev())
+    need = _lib.fa_forward_split_workspace_bytes(B, H, N, d, splits, _lib.FA_BF16)
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev())  # NaN-filled floats
+    rc = _lib.fa_forward_split(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), ws.data_ptr(), need, B, H, N, d, scale, int(causal),
+                               splits, _lib.FA_BF16, torch.cuda.current_stream().cuda_stream)
+    assert rc == _lib.FA_OK, fa.fa_strerror(rc)
+    torch.cuda.synchronize()
+    rows = B * H * N
+    po = ws[: splits * rows * d * 4].view(torch.float32).reshape(splits, B, H, N, d)
+    off = (splits * rows * d * 4 + 255) // 256 * 256
+    pl = ws[off: off + splits * rows * 4].view(torch.float32).reshape(splits, B, H, N)
+    return o.cpu(), lse.cpu(), po.cpu(), pl.cpu()
+
+
+SPLIT_CASES = [((1, 2, 300, 64), 2), ((1, 2, 300, 64), 3), ((2, 1, 1000, 64), 7),
+               ((1, 1, 77, 64), 2), ((1, 1, 100, 64), 8), ((1, 1, 129, 128), 3),
+               ((1, 2, 520, 256), 4), ((1, 1, 1, 64), 4)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape,splits", SPLIT_CASES)
+def test_split_forward_matches_oracle(shape, splits, causal):
+    B, H, N, d = shape
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, _ = make_inputs(shape, torch.bfloat16, sum(shape) + splits, 0.5 if d == 256 else 1.0)
+    o, lse, po, pl = split_raw(q, k, v, scale, causal, splits)
+    ro, rl = A.per_head(A.attention_forward, (q, k, v), scale, causal)
+    what = f"{shape} splits={splits} causal={causal}"
+    assert torch.isfinite(o.double()).all() and torch.isfinite(lse).all(), what
+    assert max_abs(o, ro) <= O_TOL, f"{what}: O {max_abs(o, ro)}"
+    assert max_abs(lse, rl) <= LSE_TOL, f"{what}: LSE {max_abs(lse, rl)}"
+    # each range's partial result against attention over that range alone
+    span = span_of(N, splits)
+    for s in range(splits):
+        lo, hi = s * span, min(N, (s + 1) * span)
+        so, sl = A.per_head(A.attention_forward_keys, (q, k, v), scale, causal, lo, hi)
+        empty = torch.isinf(sl)
+        assert torch.equal(torch.isinf(pl[s]), empty), f"{what}: range {s} empty rows differ"
+        assert float(po[s][empty].abs().max()) == 0.0 if empty.any() else True
+        full = ~empty
+        if full.any():
+            assert max_abs(po[s][full], so[full]) <= O_TOL, f"{what}: range {s} O"
+            assert max_abs(pl[s][full], sl[full]) <= LSE_TOL, f"{what}: range {s} LSE"
+
+
+def test_split_one_is_the_plain_forward():
+    q, k, v, _ = make_inputs((2, 3, 200, 64), torch.bfloat16, 3)
+    qd, kd, vd = (t.to(dev()) for t in (q, k, v))
+    o1, l1 = fa.forward(qd, kd, vd, 0.125, True)
+    o2, l2 = fa.forward_split(qd, kd, vd, 0.125, True, splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_split_deterministic():
+    q, k, v, _ = make_inputs((1, 4, 700, 64), torch.bfloat16, 4)
+    qd, kd, vd = (t.to(dev()) for t in (q, k, v))
+    a = fa.forward_split(qd, kd, vd, 0.125, False, splits=5)
+    b = fa.forward_split(qd, kd, vd, 0.125, False, splits=5)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_merge_partials_matches_oracle(dtype, d):
+    S, B, H, N = 5, 2, 3, 37
+    g = torch.Generator("cpu").manual_seed(d + (dtype == torch.float32))
+    lse = torch.randn((S, B, H, N), generator=g) * 4
+    lse[1, 0, 0, :7] = -math.inf
+    lse[:, 1, 2, 5] = -math.inf          # a row with every part empty
+    lse[3, :, 1, :] = -math.inf
+    po = torch.randn((S, B, H, N, d), generator=g) * 0.5
+    po[torch.isinf(lse)] = float("nan")  # an empty part's output must not be read
+    o, l = fa.merge_partials(po.to(dev()).contiguous(), lse.to(dev()).contiguous(), dtype)
+    torch.cuda.synchronize()
+    rl, ro = OS.merge_parts(lse.double(), torch.nan_to_num(po.double(), nan=0.0))
+    o, l = o.cpu().double(), l.cpu().double()
+    empty = torch.isinf(rl)
+    assert torch.equal(torch.isinf(l), empty)
+    assert float(o[empty].abs().max()) == 0.0
+    tol_o = 1e-5 if dtype == torch.float32 else 1e-2
+    assert max_abs(o[~empty], ro[~empty]) <= tol_o
+    assert max_abs(l[~empty], rl[~empty]) <= 1e-5
+
+
+@pytest.fixture(scope="module")
+def few_heads_run():
+    w = WORKLOADS["few_heads"]
+    q, k, v, do = workload_inputs(w)
+    qd, kd, vd = (t.to(dev()) for t in (q, k, v))
+    o, lse = fa.forward_split(qd, kd, vd, w.scale, w.causal, splits=4)
+    torch.cuda.synchronize()
+    return w, (q, k, v, do), o.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("h", [0, 3, 7])
+def test_few_heads_workload_sampled(few_heads_run, h):
+    w, (q, k, v, do), o, lse = few_heads_run
+    qi, _ = sample_rows(w.seed, 0, h, w.H, w.N)
+    ro, rl, _ = SM.query_rows(q[0, h], k[0, h], v[0, h], do[0, h], qi, w.scale, w.causal)
+    assert max_abs(o[0, h][qi], ro) <= O_TOL
+    assert max_abs(lse[0, h][qi], rl) <= LSE_TOL

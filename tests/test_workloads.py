@@ -24,7 +24,7 @@ def test_draw_order_and_rounding():
 
 
 def test_workload_table():
-    assert set(W.WORKLOADS) == {"tiny", "gpt2_medium", "memory", "long", "big_d"}
+    assert set(W.WORKLOADS) == {"tiny", "gpt2_medium", "memory", "long", "big_d", "few_heads"}
     g = W.WORKLOADS["gpt2_medium"]
     assert (g.B, g.H, g.N, g.d, g.causal, g.scale) == (64, 16, 1024, 64, True, 0.125)
     assert W.WORKLOADS["tiny"].dtype == torch.float32
