@@ -31,6 +31,8 @@ __all__ = [
     "attention_forward_keys",
     "attention_backward",
     "attention_forward_backward",
+    "visible_from_blocks",
+    "attention_forward_backward_masked",
     "per_head",
 ]
 
@@ -154,6 +156,44 @@ def attention_forward_backward(q, k, v, do, scale: float, causal: bool = False):
     dsum = (p * dp).sum(dim=-1, keepdim=True)
     ds = p * (dp - dsum)
     del p, dp
+    dq = scale * (ds @ k)
+    dk = scale * (ds.transpose(-1, -2) @ q)
+    return o, lse, dq, dk, dv
+
+
+def visible_from_blocks(block_mask, n: int, block: int) -> torch.Tensor:
+    """Element visibility [n, n] of a block mask [nb, nb] of block x block tiles.
+
+    Block-sparse attention ("FlashAttention and GPU memory", section 10;
+    CS324 Lecture 8, section 5.7): query i may see key j only if the tile
+    (i // block, j // block) is set.
+    """
+    bm = torch.as_tensor(block_mask) != 0
+    idx = torch.arange(n) // block
+    return bm[idx.unsqueeze(1), idx.unsqueeze(0)]
+
+
+def attention_forward_backward_masked(q, k, v, do, scale: float, causal: bool, visible):
+    """Standard attention and its chain-rule backward with an extra mask (fp64).
+
+    Scores with ``visible[i, j]`` False are -inf, like future keys, before
+    the softmax; everything else is ``attention_forward_backward``.  A row
+    that sees no key at all has nothing to normalise: its O is 0, its LSE
+    -inf and it contributes nothing to any gradient (its dQ is 0).
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    s = scores(q, k, scale, causal).masked_fill(~torch.as_tensor(visible), float("-inf"))
+    m = s.max(dim=-1).values
+    empty = m == float("-inf")
+    e = torch.exp(s - torch.where(empty, torch.zeros_like(m), m).unsqueeze(-1))
+    l = e.sum(dim=-1)
+    p = e / torch.where(empty, torch.ones_like(l), l).unsqueeze(-1)
+    o = p @ v
+    lse = torch.where(empty, torch.full_like(m, float("-inf")), m + torch.log(l))
+    dv = p.transpose(-1, -2) @ do
+    dp = do @ v.transpose(-1, -2)
+    dsum = (p * dp).sum(dim=-1, keepdim=True)
+    ds = p * (dp - dsum)
     dq = scale * (ds @ k)
     dk = scale * (ds.transpose(-1, -2) @ q)
     return o, lse, dq, dk, dv

@@ -73,8 +73,15 @@ def _mask_block(s, i0, j0, causal):
     return s.masked_fill(kj > qi, float("-inf"))
 
 
-def forward_outer_kv(q, k, v, scale, causal, br, bc, io: IOCount | None = None):
-    """Tiled forward, K/V outer loop; returns (O, m, l) for one head [N, d]."""
+def forward_outer_kv(q, k, v, scale, causal, br, bc, io: IOCount | None = None, block_mask=None):
+    """Tiled forward, K/V outer loop; returns (O, m, l) for one head [N, d].
+
+    ``block_mask`` ([ceil(N/br), ceil(N/bc)], optional): block-sparse
+    attention (section 5.7; "FlashAttention and GPU memory", section 10) --
+    a block pair whose entry is 0 is neither read nor computed, exactly like
+    a block in a query block's future.  A row that sees no key at all keeps
+    l = 0, m = -inf and O = 0.
+    """
     q, k, v = (t.to(_F64) for t in (q, k, v))
     n, d = q.shape
     io = io if io is not None else IOCount()
@@ -89,6 +96,8 @@ def forward_outer_kv(q, k, v, scale, causal, br, bc, io: IOCount | None = None):
         for i0 in range(0, n, br):
             i1 = min(n, i0 + br)
             if not _visible(i0, i1, j0, causal):
+                continue
+            if block_mask is not None and not block_mask[i0 // br][j0 // bc]:
                 continue
             rows = i1 - i0
             io.reads += 2 * rows * d + 2 * rows  # Q_i, O_i, l_i, m_i
@@ -105,7 +114,8 @@ def forward_outer_kv(q, k, v, scale, causal, br, bc, io: IOCount | None = None):
             a = torch.where(torch.isinf(mi), torch.zeros_like(mi), torch.exp(mi - m_new))
             b = torch.where(torch.isinf(mt), torch.zeros_like(mt), torch.exp(mt_safe - m_new))
             l_new = a * li + b * lt
-            o[i0:i1] = ((li * a).unsqueeze(1) * o[i0:i1] + b.unsqueeze(1) * (pt @ vj)) / l_new.unsqueeze(1)
+            den = torch.where(l_new > 0, l_new, torch.ones_like(l_new))
+            o[i0:i1] = ((li * a).unsqueeze(1) * o[i0:i1] + b.unsqueeze(1) * (pt @ vj)) / den.unsqueeze(1)
             l[i0:i1] = l_new
             m[i0:i1] = m_new
             io.writes += rows * d + 2 * rows  # O_i, l_i, m_i

@@ -352,3 +352,80 @@ def test_key_parts_merged_equal_whole_row_attention(causal):
     if causal:
         # row 3 sees no key of the range [17, 40): O = 0, LSE = -inf there
         assert parts[1][1][3].item() == -math.inf and float(parts[1][0][3].abs().max()) == 0.0
+
+
+# --------------------------------------------------------------------------
+# block-sparse attention ("FlashAttention and GPU memory" section 10; CS324
+# Lecture 8 section 5.7: causal attention is the block mask of the lower
+# triangle, 136 of 256 blocks at 16 x 16)
+
+def test_causal_is_a_block_mask_page_count():
+    rows = [r for r in read_golden("io_counts.txt") if r[0] == "causal_blocks"][0]
+    nblk, needed = int(rows[1]), int(rows[2])
+    n, d = 256, 32
+    blk = n // nblk
+    bm = torch.ones(nblk, nblk, dtype=torch.int32).tril()
+    assert int(bm.sum()) == needed
+    q, k, v = (rnd((n, d), s) for s in range(160, 163))
+    io = T.IOCount()
+    o1, m1, l1 = T.forward_outer_kv(q, k, v, 0.2, True, blk, blk, io, block_mask=bm)
+    assert io.pairs == needed
+    o_ref, lse_ref = A.attention_forward(q, k, v, 0.2, True)
+    # the pages' demo: block-sparse output equal to dense within ~1e-15
+    assert float((o1 - o_ref).abs().max()) < 1e-14
+    assert float((m1 + torch.log(l1) - lse_ref).abs().max()) < 1e-14
+
+
+def test_masked_oracle_with_full_mask_is_the_dense_oracle():
+    q, k, v, do = (rnd((2, 40, 8), s) for s in range(170, 174))
+    vis = A.visible_from_blocks(torch.ones(3, 3, dtype=torch.int32), 40, 16)
+    for causal in (False, True):
+        got = A.attention_forward_backward_masked(q, k, v, do, 0.3, causal, vis)
+        ref = A.attention_forward_backward(q, k, v, do, 0.3, causal)
+        for a, b in zip(got, ref):
+            assert torch.allclose(a, b, atol=1e-15, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_tiled_model_equals_masked_definition(causal):
+    n, d, blk = 100, 16, 16                    # 7 x 7 blocks, ragged last block
+    g = torch.Generator().manual_seed(3)
+    bm = (torch.rand(7, 7, generator=g) < 0.5).to(torch.int32)
+    bm[2, :] = 0                                # a block row that sees nothing
+    bm[0, 0] = bm[5, 0] = 1
+    q, k, v, do = (rnd((n, d), s) for s in range(180, 184))
+    vis = A.visible_from_blocks(bm, n, blk)
+    o_ref, lse_ref, dq, dk, dv = A.attention_forward_backward_masked(q, k, v, do, 0.35, causal, vis)
+    o1, m1, l1 = T.forward_outer_kv(q, k, v, 0.35, causal, blk, blk, block_mask=bm)
+    seen = l1 > 0
+    assert torch.equal(seen, torch.isfinite(lse_ref))
+    assert float((o1 - o_ref).abs().max()) < 1e-14
+    assert float((m1[seen] + torch.log(l1[seen]) - lse_ref[seen]).abs().max()) < 1e-14
+    # rows 32..47 see nothing: O = 0, LSE = -inf, dQ = 0
+    assert float(o_ref[32:48].abs().max()) == 0.0 and bool(torch.isinf(lse_ref[32:48]).all())
+    assert float(dq[32:48].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_gradients_match_central_differences(causal):
+    n, d = 6, 3
+    bm = torch.tensor([[1, 0, 1], [0, 0, 0], [1, 1, 0]], dtype=torch.int32)   # 2 x 2 tiles
+    vis = A.visible_from_blocks(bm, n, 2)
+    q, k, v, do = (rnd((n, d), s) for s in range(190, 194))
+    scale = 0.8
+
+    def loss(qq, kk, vv):
+        return float((A.attention_forward_backward_masked(qq, kk, vv, do, scale, causal, vis)[0] * do).sum())
+
+    grads = A.attention_forward_backward_masked(q, k, v, do, scale, causal, vis)[2:]
+    h = 1e-6
+    for which, gr in enumerate(grads):
+        num = torch.zeros_like(gr)
+        for idx in range(gr.numel()):
+            args = [q.clone(), k.clone(), v.clone()]
+            args[which].view(-1)[idx] += h
+            up = loss(*args)
+            args[which].view(-1)[idx] -= 2 * h
+            dn = loss(*args)
+            num.view(-1)[idx] = (up - dn) / (2 * h)
+        assert float((num - gr).abs().max()) / max(1.0, float(num.abs().max())) <= 1e-6, which
