@@ -45,6 +45,9 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2_medium")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward kernel")
+    ap.add_argument("--mask", choices=("none", "band"), default="none",
+                    help="block-sparse attention through fa_forward_sparse / fa_backward_sparse "
+                         "with a 128x128 tile mask: 'band' = tiles within two of the diagonal")
     ap.add_argument("--splits", type=int, default=1,
                     help="forward through fa_forward_split with this many key ranges "
                          "(implies --fwd-only when > 1)")
@@ -70,6 +73,35 @@ def visible_pairs(w) -> int:
     """(query, key) pairs that contribute, over all heads."""
     per_head = w.N * (w.N + 1) // 2 if w.causal else w.N * w.N
     return w.B * w.H * per_head
+
+
+def band_mask(N):
+    """Tile mask of a sliding window: tiles with |I - J| <= 2 (int32, CPU).
+
+    Every tile row and column holds at most five set tiles, so the work of
+    the workgroups (one per tile row in the forward and dQ kernels, one per
+    tile column in the dK/dV kernel) stays balanced.
+    """
+    import torch
+
+    nb = (N + 127) // 128
+    i = torch.arange(nb)
+    return ((i.unsqueeze(1) - i.unsqueeze(0)).abs() <= 2).to(torch.int32)
+
+
+def mask_pairs(w, mask) -> int:
+    """Visible (query, key) pairs of a tile mask, over all heads."""
+    import torch
+
+    N = w.N
+    sizes = torch.tensor([min(128, N - 128 * t) for t in range(mask.shape[0])], dtype=torch.int64)
+    full = (mask.to(torch.int64) * sizes.unsqueeze(1) * sizes.unsqueeze(0))
+    if w.causal:
+        # diagonal tiles keep their lower triangle only; tiles above it vanish
+        tri = torch.tril(torch.ones_like(full))
+        diag = torch.diag(torch.diagonal(mask).to(torch.int64) * sizes * (sizes + 1) // 2)
+        full = full * tri - torch.diag(torch.diag(full)) + diag
+    return int(full.sum()) * w.B * w.H
 
 
 def credited_flops(w):
@@ -191,6 +223,8 @@ def main(argv=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    sparse = args.mask != "none"
+    maskd = band_mask(N).to(dev) if sparse else None
     wsb = fa.workspace_bytes(B, H, N, d, w.dtype)
     if args.splits > 1:
         wsb = max(wsb, _lib.fa_forward_split_workspace_bytes(B, H, N, d, args.splits, dt))
@@ -207,6 +241,17 @@ def main(argv=None):
         """One step; if `ev` is given, record events between the kernels."""
         rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
         rec(0)
+        if sparse:
+            call(_lib.fa_forward_sparse(P[0], P[1], P[2], P[3], P[4], maskd.data_ptr(), B, H, N,
+                                        d, w.scale, int(w.causal), dt, sp), "fa_forward_sparse")
+            rec(1)
+            if args.fwd_only:
+                return
+            call(_lib.fa_backward_sparse(P[0], P[1], P[2], P[3], P[5], P[4], maskd.data_ptr(),
+                                         P[6], P[7], P[8], P[9], wsb, B, H, N, d, w.scale,
+                                         int(w.causal), dt, sp), "fa_backward_sparse")
+            rec(2)
+            return
         if args.splits > 1:
             call(_lib.fa_forward_split(P[0], P[1], P[2], P[3], P[4], P[9], wsb, B, H, N, d,
                                        w.scale, int(w.causal), args.splits, dt, sp),
@@ -229,7 +274,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
 
-    nev = 2 if args.fwd_only else 4
+    nev = 2 if args.fwd_only else (3 if sparse else 4)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -242,15 +287,25 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    names = ("fwd_split",) if args.splits > 1 else KERNELS[: nev - 1]
+    names = (("fwd_split",) if args.splits > 1 else
+             ("fwd_sparse", "bwd_sparse")[: nev - 1] if sparse else KERNELS[: nev - 1])
     per_kernel = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                   for i, n in enumerate(names)}
 
     fwd_fl, bwd_fl = credited_flops(w)
+    if sparse:
+        fwd_fl = 4 * w.d * mask_pairs(w, band_mask(N))
+        bwd_fl = fwd_fl * 5 // 2
     total_fl = fwd_fl if args.fwd_only else fwd_fl + bwd_fl
     tflops = total_fl / (ms_step * 1e-3) / 1e12
     dom = max(per_kernel, key=per_kernel.get)
-    bound, amount, _ = algorithmic(w, dom, 2 if dtype_name == "bf16" else 4)
+    if sparse:
+        # the forward's two contractions (fwd_sparse), or dQ's three plus dK/dV's four, per
+        # visible pair of the mask
+        per = 2 if dom == "fwd_sparse" else 7
+        bound, amount = "mfma", per * 2 * w.d * mask_pairs(w, band_mask(N))
+    else:
+        bound, amount, _ = algorithmic(w, dom, 2 if dtype_name == "bf16" else 4)
     dur_s = per_kernel[dom] * 1e-3
     if bound == "mfma":
         achieved, peak, unit = amount / dur_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
@@ -260,7 +315,8 @@ def main(argv=None):
     result = {
         "metric": METRIC if (args.workload == "gpt2_medium" and not args.fwd_only)
         else (f"attention {'fwd' if args.fwd_only else 'fwd+bwd'} TFLOP/s ({args.workload}"
-              + (f", {args.splits} key ranges)" if args.splits > 1 else ")")),
+              + (f", {args.splits} key ranges)" if args.splits > 1 else
+                 ", block-sparse band tiles, FLOPs of visible pairs)" if sparse else ")")),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -275,6 +331,8 @@ def main(argv=None):
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                    "scale": w.scale, "input_dtype": dtype_name,
                    "step": "forward" if args.fwd_only else "forward+backward",
+                   **({"tile_mask": "band |I-J|<=2", "visible_pairs": mask_pairs(w, band_mask(N))}
+                      if sparse else {}),
                    **({"splits": args.splits} if args.splits > 1 else {})},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
@@ -291,7 +349,7 @@ def main(argv=None):
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not sparse and args.splits == 1:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0

@@ -35,6 +35,9 @@ SIGNATURES = {
     "fa_forward_split_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "fa_forward_split": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I, _I, _I, _I, _F, _I, _I, _I, _VP]),
     "fa_merge_partials": (_I, [_VP, _VP, _I, _VP, _VP, _I, _I, _I, _I, _I, _VP]),
+    "fa_forward_sparse": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _F, _I, _I, _VP]),
+    "fa_backward_sparse": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
+                                _I, _I, _I, _I, _F, _I, _I, _VP]),
     "fa_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_backward": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                          _I, _I, _I, _I, _F, _I, _I, _VP]),
@@ -105,6 +108,21 @@ def fa_merge_partials(O_parts, LSE_parts, splits, O, LSE, B, H, N, d, dtype, str
     """Raw call: device pointers as ints, returns the C return code."""
     return int(load().fa_merge_partials(O_parts, LSE_parts, int(splits), O, LSE, B, H, N, d,
                                         int(dtype), stream))
+
+
+def fa_forward_sparse(Q, K, V, O, LSE, block_mask, B, H, N, d, scale, causal, dtype,
+                      stream) -> int:
+    """Raw call: device pointers as ints, returns the C return code."""
+    return int(load().fa_forward_sparse(Q, K, V, O, LSE, block_mask, B, H, N, d, float(scale),
+                                        int(causal), int(dtype), stream))
+
+
+def fa_backward_sparse(Q, K, V, O, dO, LSE, block_mask, dQ, dK, dV, workspace, workspace_bytes,
+                       B, H, N, d, scale, causal, dtype, stream) -> int:
+    """Raw call: device pointers as ints, returns the C return code."""
+    return int(load().fa_backward_sparse(Q, K, V, O, dO, LSE, block_mask, dQ, dK, dV, workspace,
+                                         workspace_bytes, B, H, N, d, float(scale), int(causal),
+                                         int(dtype), stream))
 
 
 def fa_backward_workspace_bytes(B, H, N, d, dtype) -> int:

@@ -90,6 +90,50 @@ def merge_partials(o_parts, lse_parts, dtype=torch.bfloat16):
     return o, lse
 
 
+def _mask_check(block_mask, q):
+    N = q.shape[2]
+    nb = (N + 127) // 128
+    if (block_mask.shape != (nb, nb) or block_mask.dtype != torch.int32 or not block_mask.is_contiguous()
+            or block_mask.device != q.device):
+        raise ValueError(f"block_mask must be contiguous int32 [{nb}, {nb}] on the inputs' device")
+
+
+def forward_sparse(q, k, v, block_mask, scale: float, causal: bool = False):
+    """Block-sparse forward: (O, LSE); ``block_mask`` int32 [ceil(N/128)]^2 on the device."""
+    _check("q", q)
+    _check("k", k, q)
+    _check("v", v, q)
+    B, H, N, d, dt = _dims(q)
+    _mask_check(block_mask, q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    rc = _lib.fa_forward_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), block_mask.data_ptr(), B, H, N, d, scale,
+                                int(bool(causal)), dt, _stream(q.device))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_forward_sparse")
+    return o, lse
+
+
+def backward_sparse(q, k, v, o, do, lse, block_mask, scale: float, causal: bool = False):
+    """Block-sparse backward: (dQ, dK, dV)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, None if name == "q" else q)
+    B, H, N, d, dt = _dims(q)
+    _mask_check(block_mask, q)
+    ws = torch.empty(_lib.fa_backward_workspace_bytes(B, H, N, d, dt), dtype=torch.uint8,
+                     device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    rc = _lib.fa_backward_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 do.data_ptr(), lse.data_ptr(), block_mask.data_ptr(),
+                                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                 ws.numel(), B, H, N, d, scale, int(bool(causal)), dt,
+                                 _stream(q.device))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_backward_sparse")
+    return dq, dk, dv
+
+
 def workspace_bytes(B, H, N, d, dtype) -> int:
     return _lib.fa_backward_workspace_bytes(B, H, N, d, _DTYPES[dtype])
 

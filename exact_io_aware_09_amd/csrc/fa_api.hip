@@ -121,6 +121,45 @@ int fa_merge_partials(const float* O_parts, const float* LSE_parts, int splits, 
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_forward_sparse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                      const int* block_mask, int B, int H, int N, int d, float scale, int causal,
+                      int dtype, void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !O || !LSE || !block_mask) return FA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE) ||
+      !aligned16(block_mask))
+    return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  const fa::SparseArgs sp{block_mask, (N + 127) / 128};
+  hipError_t e = fa::launch_forward_bf16(Q, K, V, O, LSE, p, reinterpret_cast<hipStream_t>(stream), sp);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_backward_sparse(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                       const float* LSE, const int* block_mask, void* dQ, void* dK, void* dV,
+                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                       float scale, int causal, int dtype, void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !O || !dO || !LSE || !block_mask || !dQ || !dK || !dV)
+    return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d, dtype))
+    return FA_ERR_NO_WORKSPACE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(LSE) || !aligned16(block_mask) || !aligned16(dQ) || !aligned16(dK) ||
+      !aligned16(dV) || !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  const fa::SparseArgs sp{block_mask, (N + 127) / 128};
+  hipError_t e = fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV,
+                                          static_cast<float*>(workspace), p, fa::kStagesGrad,
+                                          reinterpret_cast<hipStream_t>(stream), sp);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype) {
   if (check_sizes(B, H, N, d, dtype) != FA_OK) return 0;
   // D, then LSE * log2(e) from a 256-byte aligned offset

@@ -94,14 +94,18 @@ struct DkdvCfg {
   static_assert(ST >= 2 && ST <= 3, "two or three Q/dO stages");
 };
 
-template <int D, int NW, int QB, int ST, int OCC, bool CAUSAL>
+// SPARSE: block-sparse attention; the loop visits only the query chunks of
+// the 128 x 128 tiles set in column kb of the tile mask (the key block is
+// one tile column: BK = 128); with none, dK and dV are 0.
+template <int D, int NW, int QB, int ST, int OCC, bool CAUSAL, bool SPARSE = false>
 __global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                           const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
                           const float* __restrict__ Lws, const float* __restrict__ Dws,
                           bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int BH, int N,
-                          int nkb, int G, float c, float scale) {
+                          int nkb, int G, float c, float scale, SparseArgs sp = {}) {
   using C = DkdvCfg<D, NW, QB, ST>;
+  static_assert(!SPARSE || (ST == 2 && C::BK == 128), "sparse walk: two stages, 128-key blocks");
   // per stage: Q tile, dO tile, and 64 floats each of LSE*log2e and D
   __shared__ __attribute__((aligned(16))) bf16_t q0s[C::TILE], o0s[C::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t q1s[C::TILE], o1s[C::TILE];
@@ -156,17 +160,20 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 
   const int qstart = CAUSAL ? (k0 / C::BQ) * C::BQ : 0;
   const int nchunks = (N - qstart + C::BQ - 1) / C::BQ;
+  // query chunks visited: dense from qstart, or those of the set tiles
+  const BlockWalk<C::BQ, SPARSE> walk{N, (const_int_ptr)(sp.mask + kb), sp.nb, sp.nb - 1};
+  const int ifirst = SPARSE ? walk.first(qstart) : qstart;
 
-  auto fetch = [&](int t, auto S) {
-    const int i0 = qstart + t * C::BQ;
+  auto fetch_at = [&](int i0, auto S) {
     dma_tile<D, C::BQ, C::NT>(rq, i0, qst(S), tid);
     dma_tile<D, C::BQ, C::NT>(ro, i0, ost(S), tid);
     dma_rows_f32<C::BQ>(rl, i0, lst(S), lane);
     dma_rows_f32<C::BQ>(rd, i0, dst_(S), lane);
   };
+  auto fetch = [&](int t, auto S) { fetch_at(qstart + t * C::BQ, S); };
   // The first Q/dO copies go out before K and V are read, so that the
   // latencies overlap.
-  fetch(0, std::integral_constant<int, 0>{});
+  if (ifirst >= 0) fetch_at(ifirst, std::integral_constant<int, 0>{});
   // K and V fragments: B operands of S = Q K^T and dP = dO V^T (lane = key).
   bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
   if constexpr (C::KL) {
@@ -205,10 +212,15 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     }
   }
 
-  auto step = [&](int t, auto S) {
+  // Step t on the chunk at query i0; in is the next chunk's query (SPARSE:
+  // it is copied in during this step; -1 when this is the last).
+  auto step = [&](int t, int i0, int in, auto S) {
     constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
-    if (t + ST - 1 < nchunks) fetch(t + ST - 1, std::integral_constant<int, SN>{});
-    const int i0 = qstart + t * C::BQ;
+    if constexpr (SPARSE) {
+      if (in >= 0) fetch_at(in, std::integral_constant<int, SN>{});
+    } else {
+      if (t + ST - 1 < nchunks) fetch(t + ST - 1, std::integral_constant<int, SN>{});
+    }
     // some query of the chunk sees some key of this wavefront
     const bool active = !CAUSAL || i0 + C::BQ - 1 >= k0w;
     if (active) {
@@ -311,16 +323,29 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       }
     }
     // step t+1 must be resident; later steps may still be in flight
-    if (t + 1 < nchunks) {
-      wait_vmem_tiles<C::DMA_PER_TILE, ST - 2>(min(ST - 2, nchunks - t - 2));
+    if (SPARSE ? in >= 0 : t + 1 < nchunks) {
+      wait_vmem_tiles<C::DMA_PER_TILE, ST - 2>(SPARSE ? 0 : min(ST - 2, nchunks - t - 2));
       ring_barrier();
     }
   };
-  for (int t0 = 0; t0 < nchunks; t0 += ST) {
-    step(t0, std::integral_constant<int, 0>{});
-    if (t0 + 1 < nchunks) step(t0 + 1, std::integral_constant<int, 1>{});
-    if constexpr (ST > 2) {
-      if (t0 + 2 < nchunks) step(t0 + 2, std::integral_constant<int, 2>{});
+  if constexpr (SPARSE) {
+    int i0 = ifirst, in = i0 >= 0 ? walk.next(i0) : -1;
+    for (int t = 0; i0 >= 0; t += 2) {
+      step(t, i0, in, std::integral_constant<int, 0>{});
+      if (in < 0) break;
+      i0 = in;
+      in = walk.next(i0);
+      step(t + 1, i0, in, std::integral_constant<int, 1>{});
+      i0 = in;
+      in = i0 >= 0 ? walk.next(i0) : -1;
+    }
+  } else {
+    for (int t0 = 0; t0 < nchunks; t0 += ST) {
+      step(t0, qstart + t0 * C::BQ, -1, std::integral_constant<int, 0>{});
+      if (t0 + 1 < nchunks) step(t0 + 1, qstart + (t0 + 1) * C::BQ, -1, std::integral_constant<int, 1>{});
+      if constexpr (ST > 2) {
+        if (t0 + 2 < nchunks) step(t0 + 2, qstart + (t0 + 2) * C::BQ, -1, std::integral_constant<int, 2>{});
+      }
     }
   }
 
@@ -404,14 +429,18 @@ struct DqCfg {
   static_assert(ST >= 2 && ST <= 3, "two or three K/V stages");
 };
 
-template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL>
+// SPARSE: block-sparse attention; the loop visits only the K/V blocks of
+// the 128 x 128 tiles set in row qb of the tile mask (the query block is one
+// tile row: BR = 128); with none, dQ is 0.
+template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL, bool SPARSE = false>
 __global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                         const bf16_t* __restrict__ V, const bf16_t* __restrict__ O,
                         const bf16_t* __restrict__ dO, const float* __restrict__ LSE,
                         float* __restrict__ Dws, float* __restrict__ Lws, bf16_t* __restrict__ dQ,
-                        int BH, int N, int nqb, int G, float c, float scale) {
+                        int BH, int N, int nqb, int G, float c, float scale, SparseArgs sp = {}) {
   using C = DqCfg<D, NW, RB, BC, ST>;
+  static_assert(!SPARSE || (ST == 2 && C::BR == 128), "sparse walk: two stages, 128-row query blocks");
   __shared__ __attribute__((aligned(16))) bf16_t k0s[C::TILE], v0s[C::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t k1s[C::TILE], v1s[C::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t k2s[ST > 2 ? C::TILE : 8], v2s[ST > 2 ? C::TILE : 8];
@@ -450,14 +479,18 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
 
   const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
+  // keys visited: dense from 0, or the blocks of the set tiles
+  const BlockWalk<BC, SPARSE> walk{kend, (const_int_ptr)(sp.mask + (size_t)qb * sp.nb), 1, CAUSAL ? qb : sp.nb - 1};
+  const int jfirst = SPARSE ? walk.first(0) : 0;
 
-  auto fetch = [&](int t, auto S) {
-    dma_tile<D, BC, C::NT>(rk, t * BC, kst(S), tid);
-    dma_tile<D, BC, C::NT>(rv, t * BC, vst(S), tid);
+  auto fetch_at = [&](int j0, auto S) {
+    dma_tile<D, BC, C::NT>(rk, j0, kst(S), tid);
+    dma_tile<D, BC, C::NT>(rv, j0, vst(S), tid);
   };
+  auto fetch = [&](int t, auto S) { fetch_at(t * BC, S); };
   // The first K/V copies go out before Q, dO and O are read, so that the
   // latencies overlap.
-  fetch(0, std::integral_constant<int, 0>{});
+  if (jfirst >= 0) fetch_at(jfirst, std::integral_constant<int, 0>{});
   if constexpr (C::QL) {
     // Q and dO blocks copied row-major (coalesced) into LDS, rows past N as 0
     dma_tile<D, C::BR, C::NT>(make_copy_rsrc(Q + hoff, head_bytes), q0, qsg, tid);
@@ -530,10 +563,15 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
       pin_ready(of[rb][s]);
     }
 
-  auto step = [&](int t, auto S) {
+  // Step t on the block at key j0; jn is the next block's key (SPARSE: it
+  // is copied in during this step; -1 when this is the last).
+  auto step = [&](int t, int j0, int jn, auto S) {
     constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
-    if (t + ST - 1 < ntiles) fetch(t + ST - 1, std::integral_constant<int, SN>{});
-    const int j0 = t * BC;
+    if constexpr (SPARSE) {
+      if (jn >= 0) fetch_at(jn, std::integral_constant<int, SN>{});
+    } else {
+      if (t + ST - 1 < ntiles) fetch(t + ST - 1, std::integral_constant<int, SN>{});
+    }
     const bool active = !CAUSAL || j0 <= q0w + C::RW - 1;
     if (active) {
       const bf16_t* Ks = kst(S);
@@ -613,16 +651,29 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
       }
     }
     // step t+1 must be resident; later steps may still be in flight
-    if (t + 1 < ntiles) {
-      wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - t - 2));
+    if (SPARSE ? jn >= 0 : t + 1 < ntiles) {
+      wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(SPARSE ? 0 : min(ST - 2, ntiles - t - 2));
       ring_barrier();
     }
   };
-  for (int t0 = 0; t0 < ntiles; t0 += ST) {
-    step(t0, std::integral_constant<int, 0>{});
-    if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 1>{});
-    if constexpr (ST > 2) {
-      if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>{});
+  if constexpr (SPARSE) {
+    int j0 = jfirst, jn = j0 >= 0 ? walk.next(j0) : -1;
+    for (int t = 0; j0 >= 0; t += 2) {
+      step(t, j0, jn, std::integral_constant<int, 0>{});
+      if (jn < 0) break;
+      j0 = jn;
+      jn = walk.next(j0);
+      step(t + 1, j0, jn, std::integral_constant<int, 1>{});
+      j0 = jn;
+      jn = j0 >= 0 ? walk.next(j0) : -1;
+    }
+  } else {
+    for (int t0 = 0; t0 < ntiles; t0 += ST) {
+      step(t0, t0 * BC, -1, std::integral_constant<int, 0>{});
+      if (t0 + 1 < ntiles) step(t0 + 1, (t0 + 1) * BC, -1, std::integral_constant<int, 1>{});
+      if constexpr (ST > 2) {
+        if (t0 + 2 < ntiles) step(t0 + 2, (t0 + 2) * BC, -1, std::integral_constant<int, 2>{});
+      }
     }
   }
 
@@ -668,10 +719,10 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
 }
 
 template <int D, int NWK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ, int OCCQ,
-          bool CAUSAL>
+          bool CAUSAL, bool SPARSE>
 hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                    const float* LSE, void* dQ, void* dK, void* dV, float* ws, const Problem& p,
-                   unsigned stages, hipStream_t stream) {
+                   unsigned stages, SparseArgs sp, hipStream_t stream) {
   const int BH = p.B * p.H;
   const long long rows = (long long)BH * p.N;
   const float c = p.scale * kLog2e;
@@ -692,10 +743,10 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
     const long long grid = (long long)BH * nqb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int G = head_group(OCCQ * 4 / NWQ, nqb);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, RBQ, BC, STQ, OCCQ, CAUSAL>), dim3((unsigned)grid),
-                       dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                       (const bf16_t*)O, (const bf16_t*)dO, LSE, Dws, Lws, (bf16_t*)dQ, BH, p.N, nqb,
-                       G, c, p.scale);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, RBQ, BC, STQ, OCCQ, CAUSAL, SPARSE>),
+                       dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
+                       (const bf16_t*)V, (const bf16_t*)O, (const bf16_t*)dO, LSE, Dws, Lws,
+                       (bf16_t*)dQ, BH, p.N, nqb, G, c, p.scale, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -705,10 +756,10 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
     const long long grid = (long long)BH * nkb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int G = head_group(OCCK * 4 / NWK, nkb);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, QB, STK, OCCK, CAUSAL>), dim3((unsigned)grid),
-                       dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                       (const bf16_t*)dO, (const float*)Lws, (const float*)Dws, (bf16_t*)dK,
-                       (bf16_t*)dV, BH, p.N, nkb, G, c, p.scale);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, QB, STK, OCCK, CAUSAL, SPARSE>),
+                       dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
+                       (const bf16_t*)V, (const bf16_t*)dO, (const float*)Lws, (const float*)Dws,
+                       (bf16_t*)dK, (bf16_t*)dV, BH, p.N, nkb, G, c, p.scale, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -732,11 +783,16 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
 template <int D, int NWK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ, int OCCQ>
 hipError_t run_bwd_c(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                      const float* LSE, void* dQ, void* dK, void* dV, float* ws, const Problem& p,
-                     unsigned stages, hipStream_t stream) {
-  return p.causal ? run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true>(
-                        Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, stream)
-                  : run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false>(
-                        Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, stream);
+                     unsigned stages, SparseArgs sp, hipStream_t stream) {
+  if (sp.mask != nullptr)
+    return p.causal ? run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true, true>(
+                          Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream)
+                    : run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false, true>(
+                          Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream);
+  return p.causal ? run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true, false>(
+                        Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream)
+                  : run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false, false>(
+                        Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream);
 }
 
 }  // namespace
@@ -744,14 +800,14 @@ hipError_t run_bwd_c(const void* Q, const void* K, const void* V, const void* O,
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                 float* Dws, const Problem& p, unsigned stages,
-                                hipStream_t stream) {
+                                hipStream_t stream, SparseArgs sp) {
   switch (p.d) {
     case 64:
-      return run_bwd_c<64, FA_BWD_CFG_D64>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
+      return run_bwd_c<64, FA_BWD_CFG_D64>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream);
     case 128:
-      return run_bwd_c<128, FA_BWD_CFG_D128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
+      return run_bwd_c<128, FA_BWD_CFG_D128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream);
     case 256:
-      return run_bwd_c<256, FA_BWD_CFG_D256>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream);
+      return run_bwd_c<256, FA_BWD_CFG_D256>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -123,6 +123,45 @@ __device__ __forceinline__ void grouped_order(int L, int nblk, int BH, int G, in
   rank = r / gh;
 }
 
+// Offsets of the blocks (BSZ rows or keys each, BSZ dividing 128) that a
+// workgroup visits in its main loop.  Dense: every block from `start` below
+// `end`.  Block-sparse: only the blocks inside the set 128 x 128 tiles of
+// the workgroup's row (or column) of the tile mask: tiles u <= hi, entry
+// m[u * stride] (int32; the index is uniform, so the entries are read
+// through the scalar cache).  Offsets are returned in increasing order, -1
+// after the last.
+// The mask is read-only for the whole launch: entries are loaded through
+// the constant address space, i.e. with scalar loads, which are waited on
+// with lgkmcnt and so never wait for the vector-memory copies in flight.
+typedef const __attribute__((address_space(4))) int* const_int_ptr;
+
+template <int BSZ, bool SPARSE>
+struct BlockWalk {
+  static_assert(128 % BSZ == 0, "blocks must tile the 128-wide mask tiles");
+  int end;
+  const_int_ptr m;
+  int stride, hi;
+  // first set tile at or after tile u, as an offset, or -1
+  __device__ __forceinline__ int tile_from(int u) const {
+    while (u <= hi && m[u * stride] == 0) ++u;
+    return (u <= hi && u * 128 < end) ? u * 128 : -1;
+  }
+  // `start` is a multiple of 128 when SPARSE
+  __device__ __forceinline__ int first(int start) const {
+    if constexpr (SPARSE) return tile_from(start >> 7);
+    else return start < end ? start : -1;
+  }
+  __device__ __forceinline__ int next(int off) const {
+    const int o = off + BSZ;
+    if constexpr (SPARSE) {
+      if ((o & 127) != 0 && o < end) return o;
+      return tile_from((off >> 7) + 1);
+    } else {
+      return o < end ? o : -1;
+    }
+  }
+};
+
 // 16-byte global load returning zeros when `ok` is false.
 __device__ __forceinline__ uint4 load16_or_zero(const bf16_t* p, bool ok) {
   if (ok) return *reinterpret_cast<const uint4*>(p);

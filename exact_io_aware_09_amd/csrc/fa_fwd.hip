@@ -77,13 +77,21 @@ struct FwdCfg {
 // range's partial result -- O normalised over the range (float32) and the
 // range's log-sum-exp, -inf for rows that see no key of the range -- to
 // sa.Opart / sa.Lpart, for merge_kernel to combine.
-template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL, bool SPLIT = false>
+//
+// SPARSE: block-sparse attention; the loop visits only the K/V blocks of
+// the 128 x 128 tiles set in row qb of the tile mask (the query block is one
+// tile row: BR = 128).  A query block with no set tile (in reach of the
+// causal mask) writes O = 0 and LSE = -inf.
+template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL, bool SPLIT = false,
+          bool SPARSE = false>
 __global__ __launch_bounds__(NW * 64, OCC)
 void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      const bf16_t* __restrict__ V, bf16_t* __restrict__ O,
                      float* __restrict__ LSE, int BH, int N, int nqb, int G, float c,
-                     SplitArgs sa = {}) {
+                     SplitArgs sa = {}, SparseArgs sp = {}) {
   using C = FwdCfg<D, NW, RB, BC, ST>;
+  static_assert(!(SPLIT && SPARSE), "one variant at a time");
+  static_assert(!SPARSE || (ST == 2 && C::BR == 128), "sparse walk: two stages, 128-row query blocks");
   // One LDS variable per stage and operand: with the stage a compile-time
   // constant at every access, the compiler can tell the block being read
   // from the blocks still being copied in, and inserts no wait for them.
@@ -146,13 +154,35 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     }
   }
 
-  auto fetch = [&](int t, auto S) {
-    dma_tile<D, BC, C::NT>(rk, kbase + t * BC, kst(S), tid);
-    dma_tile<D, BC, C::NT>(rv, kbase + t * BC, vst(S), tid);
+  // keys visited: dense blocks kbase + t*BC, or the blocks of the set tiles
+  const BlockWalk<BC, SPARSE> walk{kend, (const_int_ptr)(sp.mask + (size_t)qb * sp.nb), 1, CAUSAL ? qb : sp.nb - 1};
+  const int jfirst = SPARSE ? walk.first(0) : kbase;
+  if constexpr (SPARSE) {
+    if (jfirst < 0) {
+      // no set tile: every row of the block sees no key
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int query = q0w + 32 * rb + c32;
+        if (query < N) {
+          if (h == 0) LSE[(size_t)bh * N + query] = -INFINITY;
+          bf16_t* Or = O + hoff + (size_t)query * D + h * (D / 2);
+#pragma unroll
+          for (int cc = 0; cc < D / 2; cc += 8)
+            *reinterpret_cast<uint4*>(Or + cc) = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+      return;
+    }
+  }
+
+  auto fetch_at = [&](int j0, auto S) {
+    dma_tile<D, BC, C::NT>(rk, j0, kst(S), tid);
+    dma_tile<D, BC, C::NT>(rv, j0, vst(S), tid);
   };
+  auto fetch = [&](int t, auto S) { fetch_at(kbase + t * BC, S); };
   // The first K/V copies go out before Q is read, so that the latencies
   // overlap.
-  fetch(0, std::integral_constant<int, 0>{});
+  fetch_at(jfirst, std::integral_constant<int, 0>{});
   bf16x8 qf[RB][C::KSTEPS];  // B operands of S^T = K Q^T (lane = query row)
   if constexpr (C::QL) {
     // Q block copied row-major (coalesced) into LDS, rows past N as zeros
@@ -267,11 +297,16 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     return part[0];
   };
 
-  auto step = [&](int t, auto S) {
+  // Step t on the block at key j0; jn is the next block's key (SPARSE: it
+  // is copied in during this step; -1 when this is the last).
+  auto step = [&](int t, int j0, int jn, auto S) {
     constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
     // the stage of step t-1 is free (barrier at the end of the last step)
-    if (t + ST - 1 < ntiles) fetch(t + ST - 1, std::integral_constant<int, SN>{});
-    const int j0 = kbase + t * BC;
+    if constexpr (SPARSE) {
+      if (jn >= 0) fetch_at(jn, std::integral_constant<int, SN>{});
+    } else {
+      if (t + ST - 1 < ntiles) fetch(t + ST - 1, std::integral_constant<int, SN>{});
+    }
     const bool active = !CAUSAL || j0 <= q0w + C::RW - 1;
     if (active) {
       const bf16_t* Ks = kst(S);
@@ -345,16 +380,30 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
       }
     }
     // step t+1 must be resident; later steps may still be in flight
-    if (t + 1 < ntiles) {
-      wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - t - 2));
+    if (SPARSE ? jn >= 0 : t + 1 < ntiles) {
+      wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(SPARSE ? 0 : min(ST - 2, ntiles - t - 2));
       ring_barrier();
     }
   };
-  for (int t0 = 0; t0 < ntiles; t0 += ST) {
-    step(t0, std::integral_constant<int, 0>{});
-    if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 1>{});
-    if constexpr (ST > 2) {
-      if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>{});
+  if constexpr (SPARSE) {
+    int j0 = jfirst, jn = walk.next(j0);
+    for (int t = 0;; t += 2) {
+      step(t, j0, jn, std::integral_constant<int, 0>{});
+      if (jn < 0) break;
+      j0 = jn;
+      jn = walk.next(j0);
+      step(t + 1, j0, jn, std::integral_constant<int, 1>{});
+      if (jn < 0) break;
+      j0 = jn;
+      jn = walk.next(j0);
+    }
+  } else {
+    for (int t0 = 0; t0 < ntiles; t0 += ST) {
+      step(t0, kbase + t0 * BC, -1, std::integral_constant<int, 0>{});
+      if (t0 + 1 < ntiles) step(t0 + 1, kbase + (t0 + 1) * BC, -1, std::integral_constant<int, 1>{});
+      if constexpr (ST > 2) {
+        if (t0 + 2 < ntiles) step(t0 + 2, kbase + (t0 + 2) * BC, -1, std::integral_constant<int, 2>{});
+      }
     }
   }
 
@@ -431,7 +480,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 
 template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL>
 hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                   const Problem& p, hipStream_t stream) {
+                   const Problem& p, hipStream_t stream, SparseArgs sp) {
   using C = FwdCfg<D, NW, RB, BC, ST>;
   const int BH = p.B * p.H;
   const int nqb = (p.N + C::BR - 1) / C::BR;
@@ -439,17 +488,22 @@ hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* 
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = p.scale * kLog2e;
   const int G = head_group(OCC * 4 / NW, nqb);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid),
-                     dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                     (bf16_t*)O, LSE, BH, p.N, nqb, G, c);
+  if (sp.mask != nullptr)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, true>), dim3((unsigned)grid),
+                       dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                       (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, sp);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid),
+                       dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                       (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{});
   return hipGetLastError();
 }
 
 template <int D, int NW, int RB, int BC, int ST, int OCC>
 hipError_t run_fwd_c(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                     const Problem& p, hipStream_t stream) {
-  return p.causal ? run_fwd<D, NW, RB, BC, ST, OCC, true>(Q, K, V, O, LSE, p, stream)
-                  : run_fwd<D, NW, RB, BC, ST, OCC, false>(Q, K, V, O, LSE, p, stream);
+                     const Problem& p, hipStream_t stream, SparseArgs sp) {
+  return p.causal ? run_fwd<D, NW, RB, BC, ST, OCC, true>(Q, K, V, O, LSE, p, stream, sp)
+                  : run_fwd<D, NW, RB, BC, ST, OCC, false>(Q, K, V, O, LSE, p, stream, sp);
 }
 
 // Merge of partial results (CS324 notes, exercises 3 and 7, and the
@@ -579,11 +633,11 @@ hipError_t launch_merge(const float* Opart, const float* Lpart, int splits, void
 }
 
 hipError_t launch_forward_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               const Problem& p, hipStream_t stream) {
+                               const Problem& p, hipStream_t stream, SparseArgs sp) {
   switch (p.d) {
-    case 64: return run_fwd_c<64, FA_FWD_CFG_D64>(Q, K, V, O, LSE, p, stream);
-    case 128: return run_fwd_c<128, FA_FWD_CFG_D128>(Q, K, V, O, LSE, p, stream);
-    case 256: return run_fwd_c<256, FA_FWD_CFG_D256>(Q, K, V, O, LSE, p, stream);
+    case 64: return run_fwd_c<64, FA_FWD_CFG_D64>(Q, K, V, O, LSE, p, stream, sp);
+    case 128: return run_fwd_c<128, FA_FWD_CFG_D128>(Q, K, V, O, LSE, p, stream, sp);
+    case 256: return run_fwd_c<256, FA_FWD_CFG_D256>(Q, K, V, O, LSE, p, stream, sp);
     default: return hipErrorInvalidValue;
   }
 }

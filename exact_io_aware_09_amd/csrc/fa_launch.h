@@ -23,9 +23,16 @@ struct SplitArgs {
   float* Lpart = nullptr;  // [splits, B*H*N] float32
 };
 
+// Block-sparse attention: int32 tile mask [nb, nb] over 128 x 128 tiles of
+// (query rows, keys), shared by every head; nonzero = the tile is computed.
+struct SparseArgs {
+  const int* mask = nullptr;
+  int nb = 0;
+};
+
 // bfloat16 inputs, fp32 accumulation on the matrix cores.
 hipError_t launch_forward_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               const Problem& p, hipStream_t stream);
+                               const Problem& p, hipStream_t stream, SparseArgs sp = {});
 // Split forward: partial results of every key range into Opart / Lpart;
 // then the merge of `splits` partial results into O (bf16 or float32) and
 // LSE.
@@ -44,9 +51,11 @@ inline long long ws_lse_offset(long long rows) { return (rows + 63) & ~63LL; }
 //   kStageDkDv  dK, dV; reads both vectors from the workspace.
 enum : unsigned { kStagePre = 1u, kStageDq = 2u, kStageDkDv = 4u, kStagesGrad = 6u };
 
+// A non-null sp.mask selects the block-sparse instantiations.
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
-                                float* Dws, const Problem& p, unsigned stages, hipStream_t stream);
+                                float* Dws, const Problem& p, unsigned stages, hipStream_t stream,
+                                SparseArgs sp = {});
 
 // float32 throughout (vector ALU).
 hipError_t launch_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,

@@ -123,6 +123,34 @@ int fa_merge_partials(const float* O_parts, const float* LSE_parts, int splits, 
                       float* LSE, int B, int H, int N, int d, int dtype, void* stream);
 
 /*
+ * Block-sparse attention (block-sparse FlashAttention, "FlashAttention and
+ * GPU memory" section 10; CS324 notes section 5.7, where causal attention is
+ * the same idea: blocks wholly in a query block's future are neither read
+ * nor computed).  block_mask: device int32 [nb, nb], nb = ceil(N / 128),
+ * row-major, shared by every (b, h): query i may see key j only if
+ * block_mask[i / 128][j / 128] != 0, and, when causal, j <= i.  The kernels
+ * visit only the set 128 x 128 tiles (query blocks and key blocks are one
+ * tile wide), so the work and the K/V (Q/dO) traffic scale with the number
+ * of set tiles.  A row that sees no key has nothing to normalise: its O is
+ * 0, its LSE -inf, its dQ 0, and it adds nothing to dK, dV.
+ *
+ * fa_forward_sparse writes O and LSE as fa_forward does; fa_backward_sparse
+ * takes the workspace of fa_backward (fa_backward_workspace_bytes) and
+ * writes dQ, dK, dV completely.  Both need the same mask, FA_BF16
+ * (FA_ERR_UNSUPPORTED otherwise) and a 16-byte aligned block_mask; the mask
+ * is only read.  All-ones masks give fa_forward / fa_backward's results
+ * bit for bit.
+ */
+int fa_forward_sparse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                      const int* block_mask, int B, int H, int N, int d, float scale, int causal,
+                      int dtype, void* stream);
+
+int fa_backward_sparse(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                       const float* LSE, const int* block_mask, void* dQ, void* dK, void* dV,
+                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                       float scale, int causal, int dtype, void* stream);
+
+/*
  * Bytes of device workspace fa_backward needs: two float32 vectors of one
  * value per query row (B*H*N rows), each starting on a 256-byte boundary --
  * -D_i = -sum_k dO_ik O_ik (D is the vector of CS324 notes section 5.4;
