@@ -146,12 +146,46 @@ def stored_traffic(kernel, workload):
     return int(k["fetch_bytes"]) + int(k["write_bytes"])
 
 
+def cpu_baseline_sampled(w, seconds: float):
+    """Time the sampled-row oracle on query rows of the first head (N too large for S)."""
+    import torch
+
+    from exact_io_aware_09_amd.workloads import sample_rows, workload_inputs
+    from oracle import sampled as SM
+
+    q, k, v, do = (t[0, 0].clone() for t in workload_inputs(w))
+    qi, _ = sample_rows(w.seed, 0, 0, w.H, w.N)
+    done, t_used, chunk = 0, 0.0, 16
+    while t_used < seconds and done < len(qi):
+        rows = torch.as_tensor(qi[done:done + chunk])
+        t0 = time.perf_counter()
+        SM.query_rows(q, k, v, do, rows, w.scale, w.causal)
+        t_used += time.perf_counter() - t0
+        done += len(rows)
+    # credited FLOPs of those rows: forward 4d per visible pair, backward 2.5x
+    pairs = sum((int(r) + 1) if w.causal else w.N for r in qi[:done])
+    tflops = 4 * w.d * pairs * 3.5 / t_used / 1e12
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "cores": torch.get_num_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 sampled-row oracle (full score rows, O, LSE and dQ per row) on {done} "
+                   f"query rows of head 0 of the {w.name} workload (N={w.N}, d={w.d}, "
+                   f"causal={w.causal}); {t_used:.1f} s; credited FLOPs of those rows / time; "
+                   "sampled, not comparable with the full-tensor baselines"),
+    }
+
+
 def cpu_baseline(w, seconds: float):
     """Time the fp64 oracle on the first heads of the same workload."""
     import torch
 
     from exact_io_aware_09_amd.workloads import make_inputs
     from oracle import attention as A  # the baseline is the oracle itself
+
+    if w.sampled:
+        return cpu_baseline_sampled(w, seconds)
 
     # the workload's own inputs (same seed), flattened to heads
     q, k, v, do = (t.reshape(w.B * w.H, w.N, w.d) for t in make_inputs(w.shape, w.dtype, w.seed, w.mult))
