@@ -68,16 +68,19 @@ void bwd_pre_bf16_kernel(const bf16_t* __restrict__ O, const bf16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Per wavefront: 32 keys whose K and V fragments stay in VGPRs.  Per
+// dK, dV.  Per wavefront: KB blocks of 32 keys whose K and V fragments stay
+// in VGPRs; every Q, dO, LSE and D fragment read from LDS feeds the KB
+// blocks' matrix instructions.  Per
 // step: a chunk of BQ = 32*QB query rows of Q and dO, with that chunk's
 // LSE*log2(e) and -D, copied HBM -> LDS by direct buffer->LDS loads into an
 // ST-stage ring (one LDS variable per stage and operand).  Q and dO are read
 // by rows for S = Q K^T and dP = dO V^T, and through the LDS transpose unit
 // for dK^T += Q^T dS and dV^T += dO^T P.
-template <int D, int NW, int QB, int ST>
+template <int D, int NW, int KB, int QB, int ST>
 struct DkdvCfg {
   static constexpr int NT = NW * kWave;
-  static constexpr int BK = NW * 32;          // keys per workgroup
+  static constexpr int KW = KB * 32;          // keys per wavefront
+  static constexpr int BK = NW * KW;          // keys per workgroup
   static constexpr int BQ = 32 * QB;          // query rows per chunk
   static constexpr int TILE = BQ * D;
   static constexpr int KSTEPS = D / 16;
@@ -97,14 +100,14 @@ struct DkdvCfg {
 // SPARSE: block-sparse attention; the loop visits only the query chunks of
 // the 128 x 128 tiles set in column kb of the tile mask (the key block is
 // one tile column: BK = 128); with none, dK and dV are 0.
-template <int D, int NW, int QB, int ST, int OCC, bool CAUSAL, bool SPARSE = false>
+template <int D, int NW, int KB, int QB, int ST, int OCC, bool CAUSAL, bool SPARSE = false>
 __global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                           const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
                           const float* __restrict__ Lws, const float* __restrict__ Dws,
                           bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int BH, int N,
                           int nkb, int G, float c, float scale, SparseArgs sp = {}) {
-  using C = DkdvCfg<D, NW, QB, ST>;
+  using C = DkdvCfg<D, NW, KB, QB, ST>;
   static_assert(!SPARSE || (ST == 2 && C::BK == 128), "sparse walk: two stages, 128-key blocks");
   // per stage: Q tile, dO tile, and 64 floats each of LSE*log2e and D
   __shared__ __attribute__((aligned(16))) bf16_t q0s[C::TILE], o0s[C::TILE];
@@ -146,17 +149,18 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   const auto rd = make_copy_rsrc(Dws + (size_t)bh * N, (uint32_t)N * 4u);
 
   const int k0 = kb * C::BK;
-  const int k0w = k0 + w * 32;
-  const int key = k0w + c32;  // this lane's key row (MFMA column)
+  const int k0w = k0 + w * C::KW;  // this lane's key rows: k0w + 32 kk + c32 (MFMA column)
 
-  f32x16 dkacc[C::DB], dvacc[C::DB];
+  f32x16 dkacc[KB][C::DB], dvacc[KB][C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+  for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dkacc[db][r] = 0.f;
-      dvacc[db][r] = 0.f;
-    }
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dkacc[kk][db][r] = 0.f;
+        dvacc[kk][db][r] = 0.f;
+      }
 
   const int qstart = CAUSAL ? (k0 / C::BQ) * C::BQ : 0;
   const int nchunks = (N - qstart + C::BQ - 1) / C::BQ;
@@ -175,7 +179,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   // latencies overlap.
   if (ifirst >= 0) fetch_at(ifirst, std::integral_constant<int, 0>{});
   // K and V fragments: B operands of S = Q K^T and dP = dO V^T (lane = key).
-  bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
+  bf16x8 kf[KB][C::KSTEPS], vf[KB][C::KSTEPS];
   if constexpr (C::KL) {
     // K and V blocks copied row-major (coalesced) into LDS, rows past N as 0
     dma_tile<D, C::BK, C::NT>(make_copy_rsrc(K + hoff, head_bytes), k0, ksg, tid);
@@ -184,19 +188,23 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     const auto rk = make_rsrc(K + hoff, head_bytes);
     const auto rv = make_rsrc(V + hoff, head_bytes);
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
-      const uint32_t off = ((uint32_t)key * D + 16 * s + 8 * h) * 2u;
-      kf[s] = as_bf16x8(buf_load16(rk, off));
-      vf[s] = as_bf16x8(buf_load16(rv, off));
-    }
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        const uint32_t off = ((uint32_t)(k0w + 32 * kk + c32) * D + 16 * s + 8 * h) * 2u;
+        kf[kk][s] = as_bf16x8(buf_load16(rk, off));
+        vf[kk][s] = as_bf16x8(buf_load16(rv, off));
+      }
     // K and V resident here: the compiler does not count the copies, so its
     // own waits for K and V must not fall inside the loop (where they would
     // also drain the copies in flight).
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
-      pin_ready(kf[s]);
-      pin_ready(vf[s]);
-    }
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        pin_ready(kf[kk][s]);
+        pin_ready(vf[kk][s]);
+      }
   }
   if constexpr (ST > 2) {
     if (1 < nchunks) fetch(1, std::integral_constant<int, 1>{});
@@ -206,10 +214,12 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   if constexpr (C::KL) {
     // each wavefront reads (and later overwrites with dK, dV) only its rows
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
-      kf[s] = frag_rows<D>(ksg, w * 32, 16 * s, c32, h);
-      vf[s] = frag_rows<D>(vsg, w * 32, 16 * s, c32, h);
-    }
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        kf[kk][s] = frag_rows<D>(ksg, w * C::KW + 32 * kk, 16 * s, c32, h);
+        vf[kk][s] = frag_rows<D>(vsg, w * C::KW + 32 * kk, 16 * s, c32, h);
+      }
   }
 
   // Step t on the chunk at query i0; in is the next chunk's query (SPARSE:
@@ -232,7 +242,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       // S = Q K^T and dP - D = dO V^T - D (lane: key; registers: query
       // rows); the dP accumulator starts from the workspace's -D, register
       // 4g + e holding row 8g + 4h + e of the block (16-byte LDS reads).
-      f32x16 sacc[QB], pacc[QB];
+      f32x16 sacc[QB][KB], pacc[QB][KB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         f32x16 nd;
@@ -246,13 +256,16 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
         for (int s = 0; s < C::KSTEPS; ++s) {
           const bf16x8 aq = frag_rows<D>(Qs, qb * 32, 16 * s, c32, h);
           const bf16x8 ao = frag_rows<D>(Os, qb * 32, 16 * s, c32, h);
-          if (s == 0) {
-            const f32x16 z = {};
-            sacc[qb] = mfma32x32x16(aq, kf[s], z);
-            pacc[qb] = mfma32x32x16(ao, vf[s], nd);
-          } else {
-            sacc[qb] = mfma32x32x16(aq, kf[s], sacc[qb]);
-            pacc[qb] = mfma32x32x16(ao, vf[s], pacc[qb]);
+#pragma unroll
+          for (int kk = 0; kk < KB; ++kk) {
+            if (s == 0) {
+              const f32x16 z = {};
+              sacc[qb][kk] = mfma32x32x16(aq, kf[kk][s], z);
+              pacc[qb][kk] = mfma32x32x16(ao, vf[kk][s], nd);
+            } else {
+              sacc[qb][kk] = mfma32x32x16(aq, kf[kk][s], sacc[qb][kk]);
+              pacc[qb][kk] = mfma32x32x16(ao, vf[kk][s], pacc[qb][kk]);
+            }
           }
         }
       }
@@ -266,59 +279,74 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
           // rows 8g + 4h + 0..3 of this 32-row block: one 16-byte LDS read
           const f32x4 lse4 = *reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * g + 4 * h);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sacc[qb][4 * g + e] = fast_exp2(fmaf(sacc[qb][4 * g + e], c, -lse4[e]));
+          for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sacc[qb][kk][4 * g + e] = fast_exp2(fmaf(sacc[qb][kk][4 * g + e], c, -lse4[e]));
         }
       const bool tail = i0 + C::BQ > N;
-      if (tail || (CAUSAL && i0 < k0w + 31)) {
+      if (tail || (CAUSAL && i0 < k0w + C::KW - 1)) {
         keep_branch();
-        const int kqh = key - i0 - 4 * h;  // key > query  <=>  kqh > query offset
-        if (!tail) {
-          // causal diagonal only: one compare per entry
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
+        for (int kk = 0; kk < KB; ++kk) {
+          // key > query  <=>  kqh > query offset
+          const int kqh = k0w + 32 * kk + c32 - i0 - 4 * h;
+          if (!tail) {
+            // causal diagonal only: one compare per entry
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
-              if (qoff < kqh) sacc[qb][r] = 0.f;
-            }
-        } else {
-          const int nq = N - i0 - 4 * h;  // query >= N  <=>  query offset >= nq
+            for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
+              for (int r = 0; r < 16; ++r) {
+                const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
+                if (qoff < kqh) sacc[qb][kk][r] = 0.f;
+              }
+          } else {
+            const int nq = N - i0 - 4 * h;  // query >= N  <=>  query offset >= nq
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
-              if ((CAUSAL && kqh > qoff) || qoff >= nq) sacc[qb][r] = 0.f;
-            }
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
+                if ((CAUSAL && kqh > qoff) || qoff >= nq) sacc[qb][kk][r] = 0.f;
+              }
+          }
         }
       }
       // dS = P (dP - D); P and dS packed to bf16 as B operands (k-step
       // u = 2*qb + (g>>1) holds registers 8*(g&1) .. of block qb).
-      uint32_t pw[C::PU][4], sw[C::PU][4];
+      uint32_t pw[KB][C::PU][4], sw[KB][C::PU][4];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float dsv[4];
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dsv[e] = sacc[qb][4 * g + e] * pacc[qb][4 * g + e];
-          const int u = 2 * qb + (g >> 1), w0 = 2 * (g & 1);
-          pw[u][w0] = pack_bf16x2(sacc[qb][4 * g], sacc[qb][4 * g + 1]);
-          pw[u][w0 + 1] = pack_bf16x2(sacc[qb][4 * g + 2], sacc[qb][4 * g + 3]);
-          sw[u][w0] = pack_bf16x2(dsv[0], dsv[1]);
-          sw[u][w0 + 1] = pack_bf16x2(dsv[2], dsv[3]);
-        }
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& pr = sacc[qb][kk];
+            float dsv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dsv[e] = pr[4 * g + e] * pacc[qb][kk][4 * g + e];
+            const int u = 2 * qb + (g >> 1), w0 = 2 * (g & 1);
+            pw[kk][u][w0] = pack_bf16x2(pr[4 * g], pr[4 * g + 1]);
+            pw[kk][u][w0 + 1] = pack_bf16x2(pr[4 * g + 2], pr[4 * g + 3]);
+            sw[kk][u][w0] = pack_bf16x2(dsv[0], dsv[1]);
+            sw[kk][u][w0 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+          }
 
-      // dV^T += dO^T P,  dK^T += Q^T dS  (lane: key; registers: head dims).
+      // dV^T += dO^T P,  dK^T += Q^T dS  (lane: key; registers: head dims);
+      // each transposed Q / dO fragment feeds the KB key blocks.
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
         for (int u = 0; u < C::PU; ++u) {
           const bf16x8 ao = frag_tr<D>(Os, 16 * u, db * 32, lane);
           const bf16x8 aq = frag_tr<D>(Qs, 16 * u, db * 32, lane);
-          dvacc[db] = mfma32x32x16(ao, bf16x8_from(pw[u][0], pw[u][1], pw[u][2], pw[u][3]), dvacc[db]);
-          dkacc[db] = mfma32x32x16(aq, bf16x8_from(sw[u][0], sw[u][1], sw[u][2], sw[u][3]), dkacc[db]);
+#pragma unroll
+          for (int kk = 0; kk < KB; ++kk) {
+            dvacc[kk][db] = mfma32x32x16(
+                ao, bf16x8_from(pw[kk][u][0], pw[kk][u][1], pw[kk][u][2], pw[kk][u][3]), dvacc[kk][db]);
+            dkacc[kk][db] = mfma32x32x16(
+                aq, bf16x8_from(sw[kk][u][0], sw[kk][u][1], sw[kk][u][2], sw[kk][u][3]), dkacc[kk][db]);
+          }
         }
       }
     }
@@ -350,55 +378,65 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   }
 
   if constexpr (C::KL) {
-    // fragments (dims db*32 + 8g + 4h + 0..3 of this lane's key row) into
+    // fragments (dims db*32 + 8g + 4h + 0..3 of this lane's key rows) into
     // this wavefront's rows of the staging tiles, then out as whole rows:
     // 8 lanes per row, each store instruction writes 8 complete rows
     constexpr int CPR = D / 8;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<uint2*>(ksg + tile_off<D>(w * 32 + c32, db * 32 + 8 * g + 4 * h)) =
-            make_uint2(pack_bf16x2(dkacc[db][4 * g] * scale, dkacc[db][4 * g + 1] * scale),
-                       pack_bf16x2(dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale));
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 32 * CPR / kWave; ++i) {
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint2*>(ksg + tile_off<D>(w * C::KW + 32 * kk + c32, db * 32 + 8 * g + 4 * h)) =
+              make_uint2(pack_bf16x2(dkacc[kk][db][4 * g] * scale, dkacc[kk][db][4 * g + 1] * scale),
+                         pack_bf16x2(dkacc[kk][db][4 * g + 2] * scale, dkacc[kk][db][4 * g + 3] * scale));
+#pragma unroll
+    for (int i = 0; i < C::KW * CPR / kWave; ++i) {
       const int chunk = i * kWave + lane;
       const int r = chunk / CPR, cc = chunk % CPR;
-      const uint4 v = *reinterpret_cast<const uint4*>(ksg + tile_off<D>(w * 32 + r, cc * 8));
+      const uint4 v = *reinterpret_cast<const uint4*>(ksg + tile_off<D>(w * C::KW + r, cc * 8));
       if (k0w + r < N) *reinterpret_cast<uint4*>(dK + hoff + (size_t)(k0w + r) * D + cc * 8) = v;
     }
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<uint2*>(vsg + tile_off<D>(w * 32 + c32, db * 32 + 8 * g + 4 * h)) =
-            make_uint2(pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]),
-                       pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]));
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 32 * CPR / kWave; ++i) {
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint2*>(vsg + tile_off<D>(w * C::KW + 32 * kk + c32, db * 32 + 8 * g + 4 * h)) =
+              make_uint2(pack_bf16x2(dvacc[kk][db][4 * g], dvacc[kk][db][4 * g + 1]),
+                         pack_bf16x2(dvacc[kk][db][4 * g + 2], dvacc[kk][db][4 * g + 3]));
+#pragma unroll
+    for (int i = 0; i < C::KW * CPR / kWave; ++i) {
       const int chunk = i * kWave + lane;
       const int r = chunk / CPR, cc = chunk % CPR;
-      const uint4 v = *reinterpret_cast<const uint4*>(vsg + tile_off<D>(w * 32 + r, cc * 8));
+      const uint4 v = *reinterpret_cast<const uint4*>(vsg + tile_off<D>(w * C::KW + r, cc * 8));
       if (k0w + r < N) *reinterpret_cast<uint4*>(dV + hoff + (size_t)(k0w + r) * D + cc * 8) = v;
     }
-  } else if (key < N) {
-    bf16_t* dKr = dK + hoff + (size_t)key * D;
-    bf16_t* dVr = dV + hoff + (size_t)key * D;
+  } else {
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int kk = 0; kk < KB; ++kk) {
+      const int key = k0w + 32 * kk + c32;
+      if (key < N) {
+        bf16_t* dKr = dK + hoff + (size_t)key * D;
+        bf16_t* dVr = dV + hoff + (size_t)key * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 vk, vv;
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vk[e] = to_bf16(dkacc[db][4 * g + e] * scale);
-          vv[e] = to_bf16(dvacc[db][4 * g + e]);
-        }
-        const int col = db * 32 + 8 * g + 4 * h;
-        *reinterpret_cast<bf16x4*>(dKr + col) = vk;
-        *reinterpret_cast<bf16x4*>(dVr + col) = vv;
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 vk, vv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              vk[e] = to_bf16(dkacc[kk][db][4 * g + e] * scale);
+              vv[e] = to_bf16(dvacc[kk][db][4 * g + e]);
+            }
+            const int col = db * 32 + 8 * g + 4 * h;
+            *reinterpret_cast<bf16x4*>(dKr + col) = vk;
+            *reinterpret_cast<bf16x4*>(dVr + col) = vv;
+          }
       }
+    }
   }
 }
 
@@ -718,8 +756,8 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
   }
 }
 
-template <int D, int NWK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ, int OCCQ,
-          bool CAUSAL, bool SPARSE>
+template <int D, int NWK, int KBK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ,
+          int OCCQ, bool CAUSAL, bool SPARSE>
 hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                    const float* LSE, void* dQ, void* dK, void* dV, float* ws, const Problem& p,
                    unsigned stages, SparseArgs sp, hipStream_t stream) {
@@ -751,12 +789,12 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
     if (e != hipSuccess) return e;
   }
   if (stages & kStageDkDv) {
-    using C = DkdvCfg<D, NWK, QB, STK>;
+    using C = DkdvCfg<D, NWK, KBK, QB, STK>;
     const int nkb = (p.N + C::BK - 1) / C::BK;
     const long long grid = (long long)BH * nkb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int G = head_group(OCCK * 4 / NWK, nkb);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, QB, STK, OCCK, CAUSAL, SPARSE>),
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, KBK, QB, STK, OCCK, CAUSAL, SPARSE>),
                        dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
                        (const bf16_t*)V, (const bf16_t*)dO, (const float*)Lws, (const float*)Dws,
                        (bf16_t*)dK, (bf16_t*)dV, BH, p.N, nkb, G, c, p.scale, sp);
@@ -767,31 +805,38 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
 }
 
 // Launch configurations per head dim: dK/dV (wavefronts per workgroup,
-// 32-row query blocks per chunk, Q/dO stages, minimum wavefronts per SIMD),
-// then dQ (wavefronts per workgroup, 32-row query blocks per wavefront, keys
-// per K/V block, K/V stages, minimum wavefronts per SIMD).
+// 32-key blocks per wavefront, 32-row query blocks per chunk, Q/dO stages,
+// minimum wavefronts per SIMD), then dQ (wavefronts per workgroup, 32-row
+// query blocks per wavefront, keys per K/V block, K/V stages, minimum
+// wavefronts per SIMD).
 #ifndef FA_BWD_CFG_D64
-#define FA_BWD_CFG_D64 4, 1, 2, 2, 4, 1, 32, 2, 3
+#define FA_BWD_CFG_D64 4, 1, 1, 2, 2, 4, 1, 32, 2, 3
 #endif
 #ifndef FA_BWD_CFG_D128
-#define FA_BWD_CFG_D128 4, 1, 2, 1, 4, 1, 64, 2, 1
+#define FA_BWD_CFG_D128 4, 1, 1, 2, 1, 4, 1, 64, 2, 1
 #endif
 #ifndef FA_BWD_CFG_D256
-#define FA_BWD_CFG_D256 4, 1, 2, 1, 4, 1, 32, 2, 1
+#define FA_BWD_CFG_D256 4, 1, 1, 2, 1, 4, 1, 32, 2, 1
 #endif
 
-template <int D, int NWK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ, int OCCQ>
+template <int D, int NWK, int KBK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ,
+          int OCCQ>
 hipError_t run_bwd_c(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                      const float* LSE, void* dQ, void* dK, void* dV, float* ws, const Problem& p,
                      unsigned stages, SparseArgs sp, hipStream_t stream) {
-  if (sp.mask != nullptr)
-    return p.causal ? run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true, true>(
-                          Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream)
-                    : run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false, true>(
-                          Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream);
-  return p.causal ? run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true, false>(
+  if (sp.mask != nullptr) {
+    // the sparse walk takes 128-key and 128-row blocks in two stages
+    if constexpr (NWK * KBK * 32 == 128 && STK == 2 && NWQ * RBQ * 32 == 128 && STQ == 2)
+      return p.causal ? run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true, true>(
+                            Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream)
+                      : run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false, true>(
+                            Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream);
+    else
+      return hipErrorNotSupported;
+  }
+  return p.causal ? run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true, false>(
                         Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream)
-                  : run_bwd<D, NWK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false, false>(
+                  : run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false, false>(
                         Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream);
 }
 
