@@ -21,6 +21,10 @@ tiled          the tiled forward (outer loop over K/V blocks, inner over Q
                recomputing backward, as fp64 models of the algorithm.
 io_model       element counts of HBM traffic for standard and tiled attention
                and FLOP counts.
+philox         the Philox4x32-10 counter-based generator (Salmon et al., SC 2011).
+dropout        the 8-bit draws of every (query, key) pair, the keep masks, and
+               attention with dropout on the softmax weights, forward and
+               backward, fp64.
 
 Sources: "Lecture 8 . GPU Performance & FlashAttention" (CS324 notes,
 semidirectx.com), "Stanford CS336 Lecture 5: GPUs" (chengshu blog, section 7)
