@@ -7,15 +7,18 @@ tensor wrappers (``attention.forward`` / ``attention.backward``) and the
 seeded synthetic workloads (``workloads``).
 """
 from ._lib import (FA_BF16, FA_F32, FAError, fa_backward, fa_backward_workspace_bytes,  # noqa: F401
-                   fa_backward_sparse, fa_forward, fa_forward_sparse, fa_forward_split,
+                   fa_backward_dropout, fa_backward_sparse, fa_forward, fa_forward_dropout,
+                   fa_forward_sparse, fa_forward_split,
                    fa_forward_split_workspace_bytes, fa_merge_partials, fa_strerror, fa_version)
-from .attention import (backward, backward_sparse, forward, forward_sparse,  # noqa: F401
-                        forward_split, merge_partials, workspace_bytes)
+from .attention import (backward, backward_dropout, backward_sparse, forward,  # noqa: F401
+                        forward_dropout, forward_sparse, forward_split, merge_partials,
+                        workspace_bytes)
 
 __all__ = [
     "FA_BF16", "FA_F32", "FAError", "fa_forward", "fa_backward", "fa_backward_workspace_bytes",
     "fa_strerror", "fa_version", "forward", "backward", "workspace_bytes",
     "fa_forward_split", "fa_forward_split_workspace_bytes", "fa_merge_partials",
     "forward_split", "merge_partials", "fa_forward_sparse", "fa_backward_sparse",
-    "forward_sparse", "backward_sparse",
+    "forward_sparse", "backward_sparse", "fa_forward_dropout", "fa_backward_dropout",
+    "forward_dropout", "backward_dropout",
 ]

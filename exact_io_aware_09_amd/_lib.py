@@ -28,6 +28,7 @@ _VP = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
 _SZ = ctypes.c_size_t
+_U64 = ctypes.c_ulonglong
 SIGNATURES = {
     "fa_version": (_I, []),
     "fa_strerror": (ctypes.c_char_p, [_I]),
@@ -38,6 +39,9 @@ SIGNATURES = {
     "fa_forward_sparse": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _F, _I, _I, _VP]),
     "fa_backward_sparse": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                                 _I, _I, _I, _I, _F, _I, _I, _VP]),
+    "fa_forward_dropout": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _F, _I, _F, _U64, _I, _VP]),
+    "fa_backward_dropout": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
+                                 _I, _I, _I, _I, _F, _I, _F, _U64, _I, _VP]),
     "fa_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_backward": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                          _I, _I, _I, _I, _F, _I, _I, _VP]),
@@ -123,6 +127,21 @@ def fa_backward_sparse(Q, K, V, O, dO, LSE, block_mask, dQ, dK, dV, workspace, w
     return int(load().fa_backward_sparse(Q, K, V, O, dO, LSE, block_mask, dQ, dK, dV, workspace,
                                          workspace_bytes, B, H, N, d, float(scale), int(causal),
                                          int(dtype), stream))
+
+
+def fa_forward_dropout(Q, K, V, O, LSE, B, H, N, d, scale, causal, p_drop, seed, dtype,
+                       stream) -> int:
+    """Raw call: device pointers as ints, returns the C return code."""
+    return int(load().fa_forward_dropout(Q, K, V, O, LSE, B, H, N, d, float(scale), int(causal),
+                                         float(p_drop), int(seed), int(dtype), stream))
+
+
+def fa_backward_dropout(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H, N, d,
+                        scale, causal, p_drop, seed, dtype, stream) -> int:
+    """Raw call: device pointers as ints, returns the C return code."""
+    return int(load().fa_backward_dropout(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace,
+                                          workspace_bytes, B, H, N, d, float(scale), int(causal),
+                                          float(p_drop), int(seed), int(dtype), stream))
 
 
 def fa_backward_workspace_bytes(B, H, N, d, dtype) -> int:

@@ -134,6 +134,41 @@ def backward_sparse(q, k, v, o, do, lse, block_mask, scale: float, causal: bool 
     return dq, dk, dv
 
 
+def forward_dropout(q, k, v, scale: float, causal: bool, p_drop: float, seed: int):
+    """Forward with dropout on the weights: (O, LSE); bfloat16 [B, H, N, d] inputs."""
+    _check("q", q)
+    _check("k", k, q)
+    _check("v", v, q)
+    B, H, N, d, dt = _dims(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    rc = _lib.fa_forward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr(), B, H, N, d, scale, int(bool(causal)), p_drop,
+                                 seed, dt, _stream(q.device))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_forward_dropout")
+    return o, lse
+
+
+def backward_dropout(q, k, v, o, do, lse, scale: float, causal: bool, p_drop: float, seed: int):
+    """Backward of ``forward_dropout`` with the same p_drop and seed: (dQ, dK, dV)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, None if name == "q" else q)
+    B, H, N, d, dt = _dims(q)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    ws = torch.empty(_lib.fa_backward_workspace_bytes(B, H, N, d, dt), dtype=torch.uint8,
+                     device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    rc = _lib.fa_backward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), ws.data_ptr(), ws.numel(), B, H, N, d, scale,
+                                  int(bool(causal)), p_drop, seed, dt, _stream(q.device))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_backward_dropout")
+    return dq, dk, dv
+
+
 def workspace_bytes(B, H, N, d, dtype) -> int:
     return _lib.fa_backward_workspace_bytes(B, H, N, d, _DTYPES[dtype])
 

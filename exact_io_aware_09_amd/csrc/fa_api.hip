@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -34,6 +34,19 @@ int check_common(int B, int H, int N, int d, float scale, int causal, int dtype)
   return FA_OK;
 }
 
+// Dropout: keep threshold t = round((1 - p) * 256) on the 8-bit draws,
+// 1 <= t <= 256 (p in [0, 1) and not so close to 1 that nothing is kept).
+int make_drop(float p_drop, unsigned long long seed, fa::DropArgs& dr) {
+  if (!isfinite(p_drop) || p_drop < 0.f || p_drop >= 1.f) return FA_ERR_INVALID_ARG;
+  const int t = (int)floor((1.0 - (double)p_drop) * 256.0 + 0.5);
+  if (t < 1 || t > 256) return FA_ERR_INVALID_ARG;
+  dr.k0 = (uint32_t)seed;
+  dr.k1 = (uint32_t)(seed >> 32);
+  dr.thresh = t;
+  dr.scale = (float)(256.0 / t);
+  dr.keep = (float)(t / 256.0);
+  return FA_OK;
+}
 constexpr int kMaxSplits = 256;
 
 // Split-forward workspace: the partial outputs [splits, rows, d], then the
@@ -160,6 +173,46 @@ int fa_backward_sparse(const void* Q, const void* K, const void* V, const void* 
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_forward_dropout(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                       int H, int N, int d, float scale, int causal, float p_drop,
+                       unsigned long long seed, int dtype, void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  fa::DropArgs dr;
+  rc = make_drop(p_drop, seed, dr);
+  if (rc != FA_OK) return rc;
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  hipError_t e = fa::launch_forward_dropout_bf16(Q, K, V, O, LSE, p, dr, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+int fa_backward_dropout(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                        const float* LSE, void* dQ, void* dK, void* dV, void* workspace,
+                        size_t workspace_bytes, int B, int H, int N, int d, float scale,
+                        int causal, float p_drop, unsigned long long seed, int dtype,
+                        void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  fa::DropArgs dr;
+  rc = make_drop(p_drop, seed, dr);
+  if (rc != FA_OK) return rc;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d, dtype))
+    return FA_ERR_NO_WORKSPACE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) ||
+      !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  hipError_t e = fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV,
+                                          static_cast<float*>(workspace), p, fa::kStagesGrad,
+                                          reinterpret_cast<hipStream_t>(stream), fa::SparseArgs{}, &dr);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype) {
   if (check_sizes(B, H, N, d, dtype) != FA_OK) return 0;
   // D, then LSE * log2(e) from a 256-byte aligned offset

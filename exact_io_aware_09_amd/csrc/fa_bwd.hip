@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "fa_device.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -100,14 +101,23 @@ struct DkdvCfg {
 // SPARSE: block-sparse attention; the loop visits only the query chunks of
 // the 128 x 128 tiles set in column kb of the tile mask (the key block is
 // one tile column: BK = 128); with none, dK and dV are 0.
-template <int D, int NW, int KB, int QB, int ST, int OCC, bool CAUSAL, bool SPARSE = false>
+//
+// DROP: dropout on the weights, the draws regenerated as in the forward,
+// with Z the keep mask: dV = (256/t) sum (Z P)^T dO, and dS = P (Z dP' 256/t
+// - D) computed as (256/t) P (Z ? dP' - D t/256 : -D t/256) by starting the
+// dP' accumulation from -D t/256; the factor 256/t of dK is part of `scale`
+// (the host passes scale * 256/t).
+template <int D, int NW, int KB, int QB, int ST, int OCC, bool CAUSAL, bool SPARSE = false,
+          bool DROP = false>
 __global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                           const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
                           const float* __restrict__ Lws, const float* __restrict__ Dws,
                           bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int BH, int N,
-                          int nkb, int G, float c, float scale, SparseArgs sp = {}) {
+                          int nkb, int G, float c, float scale, SparseArgs sp = {},
+                          DropArgs dr = {}) {
   using C = DkdvCfg<D, NW, KB, QB, ST>;
+  static_assert(!(SPARSE && DROP), "one variant at a time");
   static_assert(!SPARSE || (ST == 2 && C::BK == 128), "sparse walk: two stages, 128-key blocks");
   // per stage: Q tile, dO tile, and 64 floats each of LSE*log2e and D
   __shared__ __attribute__((aligned(16))) bf16_t q0s[C::TILE], o0s[C::TILE];
@@ -243,6 +253,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       // rows); the dP accumulator starts from the workspace's -D, register
       // 4g + e holding row 8g + 4h + e of the block (16-byte LDS reads).
       f32x16 sacc[QB][KB], pacc[QB][KB];
+      f32x16 ndq[DROP ? QB : 1];  // DROP: -D t/256, the dS factor of dropped pairs
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         f32x16 nd;
@@ -250,8 +261,9 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
         for (int g = 0; g < 4; ++g) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(ds + qb * 32 + 8 * g + 4 * h);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) nd[4 * g + e] = v[e];
+          for (int e = 0; e < 4; ++e) nd[4 * g + e] = DROP ? v[e] * dr.keep : v[e];
         }
+        if constexpr (DROP) ndq[qb] = nd;
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
           const bf16x8 aq = frag_rows<D>(Qs, qb * 32, 16 * s, c32, h);
@@ -314,6 +326,24 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       }
       // dS = P (dP - D); P and dS packed to bf16 as B operands (k-step
       // u = 2*qb + (g>>1) holds registers 8*(g&1) .. of block qb).
+      if constexpr (DROP) {
+        // pacc becomes dS (up to 256/t): P (dP' - D t/256) for kept pairs,
+        // P (-D t/256) for dropped ones; sacc becomes Z P, the weights of dV
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            uint32_t dw[4];
+            draws_key_cols(i0 + 32 * qb, k0w + 32 * kk, bh, lane, dr.k0, dr.k1, dw);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const bool k = kept(dw, r, dr.thresh);
+              const float pv = sacc[qb][kk][r];
+              pacc[qb][kk][r] = pv * (k ? pacc[qb][kk][r] : ndq[qb][r]);
+              sacc[qb][kk][r] = k ? pv : 0.f;
+            }
+          }
+      }
       uint32_t pw[KB][C::PU][4], sw[KB][C::PU][4];
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk)
@@ -324,7 +354,8 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
             const f32x16& pr = sacc[qb][kk];
             float dsv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dsv[e] = pr[4 * g + e] * pacc[qb][kk][4 * g + e];
+            for (int e = 0; e < 4; ++e)
+              dsv[e] = DROP ? pacc[qb][kk][4 * g + e] : pr[4 * g + e] * pacc[qb][kk][4 * g + e];
             const int u = 2 * qb + (g >> 1), w0 = 2 * (g & 1);
             pw[kk][u][w0] = pack_bf16x2(pr[4 * g], pr[4 * g + 1]);
             pw[kk][u][w0 + 1] = pack_bf16x2(pr[4 * g + 2], pr[4 * g + 3]);
@@ -377,6 +408,14 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     }
   }
 
+  if constexpr (DROP) {
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dvacc[kk][db][r] *= dr.scale;
+  }
   if constexpr (C::KL) {
     // fragments (dims db*32 + 8g + 4h + 0..3 of this lane's key rows) into
     // this wavefront's rows of the staging tiles, then out as whole rows:
@@ -470,14 +509,22 @@ struct DqCfg {
 // SPARSE: block-sparse attention; the loop visits only the K/V blocks of
 // the 128 x 128 tiles set in row qb of the tile mask (the query block is one
 // tile row: BR = 128); with none, dQ is 0.
-template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL, bool SPARSE = false>
+//
+// DROP: dropout on the weights, the draws regenerated as in the forward.
+// dS = P (Z dP' 256/t - D) with dP' = dO V^T and Z the keep mask, computed
+// as (256/t) P (Z ? dP' - D t/256 : -D t/256); the factor 256/t is part of
+// `scale` (the host passes scale * 256/t).
+template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL, bool SPARSE = false,
+          bool DROP = false>
 __global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                         const bf16_t* __restrict__ V, const bf16_t* __restrict__ O,
                         const bf16_t* __restrict__ dO, const float* __restrict__ LSE,
                         float* __restrict__ Dws, float* __restrict__ Lws, bf16_t* __restrict__ dQ,
-                        int BH, int N, int nqb, int G, float c, float scale, SparseArgs sp = {}) {
+                        int BH, int N, int nqb, int G, float c, float scale, SparseArgs sp = {},
+                        DropArgs dr = {}) {
   using C = DqCfg<D, NW, RB, BC, ST>;
+  static_assert(!(SPARSE && DROP), "one variant at a time");
   static_assert(!SPARSE || (ST == 2 && C::BR == 128), "sparse walk: two stages, 128-row query blocks");
   __shared__ __attribute__((aligned(16))) bf16_t k0s[C::TILE], v0s[C::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t k1s[C::TILE], v1s[C::TILE];
@@ -664,6 +711,19 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
             }
         }
       }
+      if constexpr (DROP) {
+        // dropped pairs: dP' -> 0, and D scaled by t/256 (see above)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb) {
+            uint32_t dw[4];
+            draws_query_cols(q0w + 32 * rb, j0 + 32 * kb, bh, lane, dr.k0, dr.k1, dw);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (!kept(dw, r, dr.thresh)) pacc[rb][kb][r] = 0.f;
+          }
+      }
       // dS^T = P^T (dP^T - D), packed to bf16: register r of block kb is
       // k-step 2*kb + (r>>3), element r & 7; then dQ^T += K^T dS^T (lane:
       // query; registers: head dims), each K^T fragment feeding RB blocks.
@@ -674,10 +734,11 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
         for (int rb = 0; rb < RB; ++rb) {
           uint32_t sw[4];
           const int kb = u >> 1, r0 = 8 * (u & 1);
+          const float dsub = DROP ? dd[rb] * dr.keep : dd[rb];
 #pragma unroll
           for (int e = 0; e < 8; e += 2)
-            sw[e >> 1] = pack_bf16x2(sacc[rb][kb][r0 + e] * (pacc[rb][kb][r0 + e] - dd[rb]),
-                                     sacc[rb][kb][r0 + e + 1] * (pacc[rb][kb][r0 + e + 1] - dd[rb]));
+            sw[e >> 1] = pack_bf16x2(sacc[rb][kb][r0 + e] * (pacc[rb][kb][r0 + e] - dsub),
+                                     sacc[rb][kb][r0 + e + 1] * (pacc[rb][kb][r0 + e + 1] - dsub));
           sf[rb] = bf16x8_from(sw[0], sw[1], sw[2], sw[3]);
         }
 #pragma unroll
@@ -757,13 +818,14 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
 }
 
 template <int D, int NWK, int KBK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ,
-          int OCCQ, bool CAUSAL, bool SPARSE>
+          int OCCQ, bool CAUSAL, bool SPARSE, bool DROP = false>
 hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                    const float* LSE, void* dQ, void* dK, void* dV, float* ws, const Problem& p,
-                   unsigned stages, SparseArgs sp, hipStream_t stream) {
+                   unsigned stages, SparseArgs sp, hipStream_t stream, DropArgs dr = {}) {
   const int BH = p.B * p.H;
   const long long rows = (long long)BH * p.N;
   const float c = p.scale * kLog2e;
+  const float gscale = DROP ? p.scale * dr.scale : p.scale;  // of dQ and dK
   float* Dws = ws;         // -D, one float per row
   float* Lws = ws + ws_lse_offset(rows);  // LSE * log2(e), one float per row
   if (stages & kStagePre) {
@@ -781,10 +843,10 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
     const long long grid = (long long)BH * nqb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int G = head_group(OCCQ * 4 / NWQ, nqb);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, RBQ, BC, STQ, OCCQ, CAUSAL, SPARSE>),
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, RBQ, BC, STQ, OCCQ, CAUSAL, SPARSE, DROP>),
                        dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
                        (const bf16_t*)V, (const bf16_t*)O, (const bf16_t*)dO, LSE, Dws, Lws,
-                       (bf16_t*)dQ, BH, p.N, nqb, G, c, p.scale, sp);
+                       (bf16_t*)dQ, BH, p.N, nqb, G, c, gscale, sp, dr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -794,10 +856,10 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
     const long long grid = (long long)BH * nkb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int G = head_group(OCCK * 4 / NWK, nkb);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, KBK, QB, STK, OCCK, CAUSAL, SPARSE>),
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, KBK, QB, STK, OCCK, CAUSAL, SPARSE, DROP>),
                        dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
                        (const bf16_t*)V, (const bf16_t*)dO, (const float*)Lws, (const float*)Dws,
-                       (bf16_t*)dK, (bf16_t*)dV, BH, p.N, nkb, G, c, p.scale, sp);
+                       (bf16_t*)dK, (bf16_t*)dV, BH, p.N, nkb, G, c, gscale, sp, dr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -823,7 +885,14 @@ template <int D, int NWK, int KBK, int QB, int STK, int OCCK, int NWQ, int RBQ, 
           int OCCQ>
 hipError_t run_bwd_c(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                      const float* LSE, void* dQ, void* dK, void* dV, float* ws, const Problem& p,
-                     unsigned stages, SparseArgs sp, hipStream_t stream) {
+                     unsigned stages, SparseArgs sp, hipStream_t stream, const DropArgs* dr) {
+  if (dr != nullptr) {
+    if (sp.mask != nullptr) return hipErrorNotSupported;
+    return p.causal ? run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true, false, true>(
+                          Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream, *dr)
+                    : run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false, false, true>(
+                          Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream, *dr);
+  }
   if (sp.mask != nullptr) {
     // the sparse walk takes 128-key and 128-row blocks in two stages
     if constexpr (NWK * KBK * 32 == 128 && STK == 2 && NWQ * RBQ * 32 == 128 && STQ == 2)
@@ -845,14 +914,14 @@ hipError_t run_bwd_c(const void* Q, const void* K, const void* V, const void* O,
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                 float* Dws, const Problem& p, unsigned stages,
-                                hipStream_t stream, SparseArgs sp) {
+                                hipStream_t stream, SparseArgs sp, const DropArgs* dr) {
   switch (p.d) {
     case 64:
-      return run_bwd_c<64, FA_BWD_CFG_D64>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream);
+      return run_bwd_c<64, FA_BWD_CFG_D64>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream, dr);
     case 128:
-      return run_bwd_c<128, FA_BWD_CFG_D128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream);
+      return run_bwd_c<128, FA_BWD_CFG_D128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream, dr);
     case 256:
-      return run_bwd_c<256, FA_BWD_CFG_D256>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream);
+      return run_bwd_c<256, FA_BWD_CFG_D256>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream, dr);
     default:
       return hipErrorInvalidValue;
   }

@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "fa_device.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -82,15 +83,19 @@ struct FwdCfg {
 // the 128 x 128 tiles set in row qb of the tile mask (the query block is one
 // tile row: BR = 128).  A query block with no set tile (in reach of the
 // causal mask) writes O = 0 and LSE = -inf.
+//
+// DROP: dropout on the weights.  The row sums (and so the LSE) are taken
+// before it; the dropped weights are zeroed before P V, and the kept ones
+// are scaled by 256 / t in the final division.
 template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL, bool SPLIT = false,
-          bool SPARSE = false>
+          bool SPARSE = false, bool DROP = false>
 __global__ __launch_bounds__(NW * 64, OCC)
 void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      const bf16_t* __restrict__ V, bf16_t* __restrict__ O,
                      float* __restrict__ LSE, int BH, int N, int nqb, int G, float c,
-                     SplitArgs sa = {}, SparseArgs sp = {}) {
+                     SplitArgs sa = {}, SparseArgs sp = {}, DropArgs dr = {}) {
   using C = FwdCfg<D, NW, RB, BC, ST>;
-  static_assert(!(SPLIT && SPARSE), "one variant at a time");
+  static_assert((int)SPLIT + (int)SPARSE + (int)DROP <= 1, "one variant at a time");
   static_assert(!SPARSE || (ST == 2 && C::BR == 128), "sparse walk: two stages, 128-row query blocks");
   // One LDS variable per stage and operand: with the stage a compile-time
   // constant at every access, the compiler can tell the block being read
@@ -357,6 +362,18 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) l[rb] += rs[rb];
+      if constexpr (DROP) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb) {
+            uint32_t dw[4];
+            draws_query_cols(q0w + 32 * rb, j0 + 32 * kb, bh, lane, dr.k0, dr.k1, dw);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (!kept(dw, r, dr.thresh)) sacc[rb][kb][r] = 0.f;
+          }
+      }
 
       // P^T as B operand (k-step u: registers 8*(u&1).. of key block u>>1,
       // i.e. keys 16u + 8*(e>>2) + 4h + (e&3)), rounded to bf16, then
@@ -438,7 +455,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   for (int rb = 0; rb < RB; ++rb) {
     const int query = q0w + 32 * rb + c32;
     const float lt = sum_halves(l[rb]);  // >= 1: the row maximum has weight >= 1
-    const float inv = __builtin_amdgcn_rcpf(lt);
+    const float inv = DROP ? __builtin_amdgcn_rcpf(lt) * dr.scale : __builtin_amdgcn_rcpf(lt);
     if constexpr (C::QL) {
       // O fragment (dims db*32 + 8g + 4h + 0..3 of this lane's row) into
       // this wavefront's rows of the Q staging tile
@@ -497,6 +514,30 @@ hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* 
                        dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                        (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{});
   return hipGetLastError();
+}
+
+template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL>
+hipError_t run_fwd_drop(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        const Problem& p, const DropArgs& dr, hipStream_t stream) {
+  using C = FwdCfg<D, NW, RB, BC, ST>;
+  const int BH = p.B * p.H;
+  const int nqb = (p.N + C::BR - 1) / C::BR;
+  const long long grid = (long long)BH * nqb;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const float c = p.scale * kLog2e;
+  const int G = head_group(OCC * 4 / NW, nqb);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, false, true>),
+                     dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
+                     (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{},
+                     dr);
+  return hipGetLastError();
+}
+
+template <int D, int NW, int RB, int BC, int ST, int OCC>
+hipError_t run_fwd_drop_c(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                          const Problem& p, const DropArgs& dr, hipStream_t stream) {
+  return p.causal ? run_fwd_drop<D, NW, RB, BC, ST, OCC, true>(Q, K, V, O, LSE, p, dr, stream)
+                  : run_fwd_drop<D, NW, RB, BC, ST, OCC, false>(Q, K, V, O, LSE, p, dr, stream);
 }
 
 template <int D, int NW, int RB, int BC, int ST, int OCC>
@@ -628,6 +669,17 @@ hipError_t launch_merge(const float* Opart, const float* Lpart, int splits, void
     case 64: return run_merge<64>(Opart, Lpart, splits, O, LSE, rows, bf16, stream);
     case 128: return run_merge<128>(Opart, Lpart, splits, O, LSE, rows, bf16, stream);
     case 256: return run_merge<256>(Opart, Lpart, splits, O, LSE, rows, bf16, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_forward_dropout_bf16(const void* Q, const void* K, const void* V, void* O,
+                                       float* LSE, const Problem& p, const DropArgs& dr,
+                                       hipStream_t stream) {
+  switch (p.d) {
+    case 64: return run_fwd_drop_c<64, FA_FWD_CFG_D64>(Q, K, V, O, LSE, p, dr, stream);
+    case 128: return run_fwd_drop_c<128, FA_FWD_CFG_D128>(Q, K, V, O, LSE, p, dr, stream);
+    case 256: return run_fwd_drop_c<256, FA_FWD_CFG_D256>(Q, K, V, O, LSE, p, dr, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,6 +1,7 @@
 // fa_launch.h -- host-side launchers behind the C ABI (internal, C++ linkage).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -30,9 +31,22 @@ struct SparseArgs {
   int nb = 0;
 };
 
+// Dropout on the attention weights: 64-bit generator key (k0 low word), keep
+// threshold t in 1..256 on the 8-bit draws, kept weights scaled by 256 / t.
+struct DropArgs {
+  uint32_t k0 = 0, k1 = 0;
+  int thresh = 256;
+  float scale = 1.f;  // 256 / t
+  float keep = 1.f;   // t / 256
+};
+
 // bfloat16 inputs, fp32 accumulation on the matrix cores.
 hipError_t launch_forward_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                const Problem& p, hipStream_t stream, SparseArgs sp = {});
+// With dropout (dense, not split, not sparse).
+hipError_t launch_forward_dropout_bf16(const void* Q, const void* K, const void* V, void* O,
+                                       float* LSE, const Problem& p, const DropArgs& dr,
+                                       hipStream_t stream);
 // Split forward: partial results of every key range into Opart / Lpart;
 // then the merge of `splits` partial results into O (bf16 or float32) and
 // LSE.
@@ -51,11 +65,12 @@ inline long long ws_lse_offset(long long rows) { return (rows + 63) & ~63LL; }
 //   kStageDkDv  dK, dV; reads both vectors from the workspace.
 enum : unsigned { kStagePre = 1u, kStageDq = 2u, kStageDkDv = 4u, kStagesGrad = 6u };
 
-// A non-null sp.mask selects the block-sparse instantiations.
+// A non-null sp.mask selects the block-sparse instantiations, a non-null dr
+// the dropout ones (not both).
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                 float* Dws, const Problem& p, unsigned stages, hipStream_t stream,
-                                SparseArgs sp = {});
+                                SparseArgs sp = {}, const DropArgs* dr = nullptr);
 
 // float32 throughout (vector ALU).
 hipError_t launch_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,

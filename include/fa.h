@@ -151,6 +151,50 @@ int fa_backward_sparse(const void* Q, const void* K, const void* V, const void* 
                        float scale, int causal, int dtype, void* stream);
 
 /*
+ * Attention with dropout on the weights (the fused dropout of "FlashAttention
+ * and GPU memory", section 07: applied after the softmax, before the product
+ * with V).  No mask is stored: the forward keeps only the generator's key
+ * (`seed`), and the backward regenerates the same draws ("FlashAttention and
+ * GPU memory", section 09; CS324 notes, section 5.4).
+ *
+ *   Z_ij  = [u_ij < t],  t = round((1 - p_drop) * 256)   (keep mask)
+ *   O     = (P o Z) V * 256 / t
+ *   LSE   as fa_forward (the softmax's normaliser; dropout does not touch it)
+ *
+ * u_ij (0..255) is the draw of query i and key j of head b*H + h: byte
+ * (j mod 4) of word (i mod 4) of Philox4x32-10 (Salmon et al., "Parallel
+ * random numbers: as easy as 1, 2, 3", SC 2011) at counter
+ * (j / 4, i / 4, b*H + h, 0) under key (seed mod 2^32, seed / 2^32).  So the
+ * drop probability actually applied is 1 - t/256 (p_drop rounded to a
+ * multiple of 1/256), and the kept weights are scaled so that the expected
+ * output is P V exactly.  The draws depend only on (seed, b, h, i, j): the
+ * same seed gives the same mask for any causal flag and launch
+ * configuration.
+ *
+ * fa_backward_dropout returns the gradients of L = sum(dO * O) for that O
+ * with the mask fixed:
+ *   dV = (P o Z)^T dO * 256/t,  dP = (dO V^T) o Z * 256/t,
+ *   D_i = sum_k dO_ik O_ik,  dS = P o (dP - D),  dQ = scale dS K,
+ *   dK = scale dS^T Q;
+ * it takes fa_backward's workspace and writes dQ, dK, dV completely.  Pass
+ * the seed and p_drop of the forward that produced O and LSE.
+ *
+ * p_drop: finite, 0 <= p_drop < 1 with t >= 1 (FA_ERR_INVALID_ARG
+ * otherwise); p_drop = 0 gives fa_forward / fa_backward's results bit for
+ * bit.  FA_BF16 only (FA_ERR_UNSUPPORTED otherwise).  Other arguments and
+ * errors as fa_forward / fa_backward.
+ */
+int fa_forward_dropout(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                       int H, int N, int d, float scale, int causal, float p_drop,
+                       unsigned long long seed, int dtype, void* stream);
+
+int fa_backward_dropout(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                        const float* LSE, void* dQ, void* dK, void* dV, void* workspace,
+                        size_t workspace_bytes, int B, int H, int N, int d, float scale,
+                        int causal, float p_drop, unsigned long long seed, int dtype,
+                        void* stream);
+
+/*
  * Bytes of device workspace fa_backward needs: two float32 vectors of one
  * value per query row (B*H*N rows), each starting on a 256-byte boundary --
  * -D_i = -sum_k dO_ik O_ik (D is the vector of CS324 notes section 5.4;

@@ -143,3 +143,38 @@ def test_merge_partials_validation(args, code):
               dtype=_lib.FA_BF16, stream=None)
     kw.update(args)
     assert fa.fa_merge_partials(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(p_drop=-0.1), _lib.FA_ERR_INVALID_ARG),
+    (dict(p_drop=1.0), _lib.FA_ERR_INVALID_ARG),
+    (dict(p_drop=0.999), _lib.FA_ERR_INVALID_ARG),   # round(0.256) = 0: nothing kept
+    (dict(p_drop=float("nan")), _lib.FA_ERR_INVALID_ARG),
+    (dict(dtype=_lib.FA_F32), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(V=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(O=A + 2), _lib.FA_ERR_MISALIGNED),
+    (dict(scale=0.0), _lib.FA_ERR_INVALID_ARG),
+])
+def test_forward_dropout_validation(args, code):
+    kw = dict(Q=A, K=A, V=A, O=A, LSE=A, B=1, H=1, N=128, d=64, scale=0.125, causal=0,
+              p_drop=0.1, seed=(1 << 64) - 1, dtype=_lib.FA_BF16, stream=None)
+    kw.update(args)
+    assert fa.fa_forward_dropout(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(p_drop=1.5), _lib.FA_ERR_INVALID_ARG),
+    (dict(dtype=_lib.FA_F32), _lib.FA_ERR_UNSUPPORTED),
+    (dict(workspace=0), _lib.FA_ERR_NO_WORKSPACE),
+    (dict(workspace_bytes=511), _lib.FA_ERR_NO_WORKSPACE),
+    (dict(dK=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(dQ=A + 8), _lib.FA_ERR_MISALIGNED),
+    (dict(causal=3), _lib.FA_ERR_INVALID_ARG),
+])
+def test_backward_dropout_validation(args, code):
+    kw = dict(Q=A, K=A, V=A, O=A, dO=A, LSE=A, dQ=A, dK=A, dV=A, workspace=A,
+              workspace_bytes=512, B=1, H=1, N=16, d=64, scale=0.125, causal=1, p_drop=0.2,
+              seed=7, dtype=_lib.FA_BF16, stream=None)
+    kw.update(args)
+    assert fa.fa_backward_dropout(**kw) == code
