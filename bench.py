@@ -36,6 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic.json"
 KERNELS = ("fwd", "bwd_dq", "bwd_dkdv")
+DROPOUT_SEED = 0x5EED0F00D
 
 
 def parse_args(argv=None):
@@ -51,6 +52,9 @@ def parse_args(argv=None):
     ap.add_argument("--splits", type=int, default=1,
                     help="forward through fa_forward_split with this many key ranges "
                          "(implies --fwd-only when > 1)")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="drop probability of the fused dropout (fa_forward_dropout / "
+                         "fa_backward_dropout); 0 = no dropout")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -258,6 +262,11 @@ def main(argv=None):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     sparse = args.mask != "none"
+    drop = args.dropout > 0.0
+    if drop and (sparse or args.splits > 1):
+        print("bench.py: --dropout runs the dense path only", file=sys.stderr)
+        return 2
+    fused = sparse or drop  # one backward call: events around forward and backward only
     maskd = band_mask(N).to(dev) if sparse else None
     wsb = fa.workspace_bytes(B, H, N, d, w.dtype)
     if args.splits > 1:
@@ -286,6 +295,18 @@ def main(argv=None):
                                          int(w.causal), dt, sp), "fa_backward_sparse")
             rec(2)
             return
+        if drop:
+            call(_lib.fa_forward_dropout(P[0], P[1], P[2], P[3], P[4], B, H, N, d, w.scale,
+                                         int(w.causal), args.dropout, DROPOUT_SEED, dt, sp),
+                 "fa_forward_dropout")
+            rec(1)
+            if args.fwd_only:
+                return
+            call(_lib.fa_backward_dropout(P[0], P[1], P[2], P[3], P[5], P[4], P[6], P[7], P[8],
+                                          P[9], wsb, B, H, N, d, w.scale, int(w.causal),
+                                          args.dropout, DROPOUT_SEED, dt, sp), "fa_backward_dropout")
+            rec(2)
+            return
         if args.splits > 1:
             call(_lib.fa_forward_split(P[0], P[1], P[2], P[3], P[4], P[9], wsb, B, H, N, d,
                                        w.scale, int(w.causal), args.splits, dt, sp),
@@ -308,7 +329,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
 
-    nev = 2 if args.fwd_only else (3 if sparse else 4)
+    nev = 2 if args.fwd_only else (3 if fused else 4)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -322,7 +343,8 @@ def main(argv=None):
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
     names = (("fwd_split",) if args.splits > 1 else
-             ("fwd_sparse", "bwd_sparse")[: nev - 1] if sparse else KERNELS[: nev - 1])
+             ("fwd_sparse", "bwd_sparse")[: nev - 1] if sparse else
+             ("fwd_dropout", "bwd_dropout")[: nev - 1] if drop else KERNELS[: nev - 1])
     per_kernel = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                   for i, n in enumerate(names)}
 
@@ -338,6 +360,10 @@ def main(argv=None):
         # visible pair of the mask
         per = 2 if dom == "fwd_sparse" else 7
         bound, amount = "mfma", per * 2 * w.d * mask_pairs(w, band_mask(N))
+    elif drop:
+        # as above, per visible (query, key) pair of the causal or full pattern
+        per = 2 if dom == "fwd_dropout" else 7
+        bound, amount = "mfma", per * 2 * w.d * visible_pairs(w)
     else:
         bound, amount, _ = algorithmic(w, dom, 2 if dtype_name == "bf16" else 4)
     dur_s = per_kernel[dom] * 1e-3
@@ -347,10 +373,11 @@ def main(argv=None):
         achieved, peak, unit = amount / dur_s / 1e9, PEAK_HBM_GBS, "GB/s"
 
     result = {
-        "metric": METRIC if (args.workload == "gpt2_medium" and not args.fwd_only)
+        "metric": METRIC if (args.workload == "gpt2_medium" and not args.fwd_only and not drop)
         else (f"attention {'fwd' if args.fwd_only else 'fwd+bwd'} TFLOP/s ({args.workload}"
               + (f", {args.splits} key ranges)" if args.splits > 1 else
-                 ", block-sparse band tiles, FLOPs of visible pairs)" if sparse else ")")),
+                 ", block-sparse band tiles, FLOPs of visible pairs)" if sparse else
+                 f", dropout {args.dropout})" if drop else ")")),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -367,7 +394,8 @@ def main(argv=None):
                    "step": "forward" if args.fwd_only else "forward+backward",
                    **({"tile_mask": "band |I-J|<=2", "visible_pairs": mask_pairs(w, band_mask(N))}
                       if sparse else {}),
-                   **({"splits": args.splits} if args.splits > 1 else {})},
+                   **({"splits": args.splits} if args.splits > 1 else {}),
+                   **({"dropout": args.dropout, "seed": DROPOUT_SEED} if drop else {})},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
@@ -383,7 +411,7 @@ def main(argv=None):
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and not sparse and args.splits == 1:
+    if not args.no_cpu_baseline and not fused and args.splits == 1:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
