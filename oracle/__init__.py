@@ -25,6 +25,8 @@ philox         the Philox4x32-10 counter-based generator (Salmon et al., SC 2011
 dropout        the 8-bit draws of every (query, key) pair, the keep masks, and
                attention with dropout on the softmax weights, forward and
                backward, fp64.
+fp8            the OCP E4M3 format, block quantisation with power-of-two
+               block scales, and attention of the quantised inputs, fp64.
 
 Sources: "Lecture 8 . GPU Performance & FlashAttention" (CS324 notes,
 semidirectx.com), "Stanford CS336 Lecture 5: GPUs" (chengshu blog, section 7)
