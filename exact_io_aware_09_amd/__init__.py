@@ -6,13 +6,15 @@ its ctypes binding (``_lib``: the C entry points under the same names), thin
 tensor wrappers (``attention.forward`` / ``attention.backward``) and the
 seeded synthetic workloads (``workloads``).
 """
-from ._lib import (FA_BF16, FA_F32, FAError, fa_backward, fa_backward_workspace_bytes,  # noqa: F401
-                   fa_backward_dropout, fa_backward_sparse, fa_forward, fa_forward_dropout,
-                   fa_forward_sparse, fa_forward_split,
+from ._lib import (FA_BF16, FA_F32, FA_FP8_KEYS, FA_FP8_ROWS, FAError,  # noqa: F401
+                   fa_backward, fa_backward_workspace_bytes, fa_backward_dropout,
+                   fa_backward_sparse, fa_forward, fa_forward_dropout, fa_forward_fp8,
+                   fa_forward_sparse, fa_forward_split, fa_fp8_bytes, fa_fp8_scale_bytes,
+                   fa_quantize_fp8,
                    fa_forward_split_workspace_bytes, fa_merge_partials, fa_strerror, fa_version)
 from .attention import (backward, backward_dropout, backward_sparse, forward,  # noqa: F401
-                        forward_dropout, forward_sparse, forward_split, merge_partials,
-                        workspace_bytes)
+                        forward_dropout, forward_fp8, forward_sparse, forward_split,
+                        merge_partials, quantize_fp8, workspace_bytes)
 
 __all__ = [
     "FA_BF16", "FA_F32", "FAError", "fa_forward", "fa_backward", "fa_backward_workspace_bytes",
@@ -20,5 +22,6 @@ __all__ = [
     "fa_forward_split", "fa_forward_split_workspace_bytes", "fa_merge_partials",
     "forward_split", "merge_partials", "fa_forward_sparse", "fa_backward_sparse",
     "forward_sparse", "backward_sparse", "fa_forward_dropout", "fa_backward_dropout",
-    "forward_dropout", "backward_dropout",
+    "forward_dropout", "backward_dropout", "FA_FP8_ROWS", "FA_FP8_KEYS", "fa_fp8_bytes",
+    "fa_fp8_scale_bytes", "fa_quantize_fp8", "fa_forward_fp8", "quantize_fp8", "forward_fp8",
 ]

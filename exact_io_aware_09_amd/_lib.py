@@ -16,6 +16,9 @@ LIB_PATH = Path(__file__).resolve().parent / "libfa_mi355x.so"
 FA_BF16 = 0
 FA_F32 = 1
 
+FA_FP8_ROWS = 0
+FA_FP8_KEYS = 1
+
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
@@ -42,6 +45,10 @@ SIGNATURES = {
     "fa_forward_dropout": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _F, _I, _F, _U64, _I, _VP]),
     "fa_backward_dropout": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                                  _I, _I, _I, _I, _F, _I, _F, _U64, _I, _VP]),
+    "fa_fp8_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "fa_fp8_scale_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "fa_quantize_fp8": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, _VP]),
+    "fa_forward_fp8": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _F, _I, _VP]),
     "fa_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_backward": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                          _I, _I, _I, _I, _F, _I, _I, _VP]),
@@ -142,6 +149,25 @@ def fa_backward_dropout(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_by
     return int(load().fa_backward_dropout(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace,
                                           workspace_bytes, B, H, N, d, float(scale), int(causal),
                                           float(p_drop), int(seed), int(dtype), stream))
+
+
+def fa_fp8_bytes(B, H, N, d, layout) -> int:
+    return int(load().fa_fp8_bytes(B, H, N, d, int(layout)))
+
+
+def fa_fp8_scale_bytes(B, H, N, d, layout) -> int:
+    return int(load().fa_fp8_scale_bytes(B, H, N, d, int(layout)))
+
+
+def fa_quantize_fp8(X, X8, Xs, B, H, N, d, layout, stream) -> int:
+    """Raw call: device pointers as ints, returns the C return code."""
+    return int(load().fa_quantize_fp8(X, X8, Xs, B, H, N, d, int(layout), stream))
+
+
+def fa_forward_fp8(Q8, Qs, K8, Ks, V8, Vs, O, LSE, B, H, N, d, scale, causal, stream) -> int:
+    """Raw call: device pointers as ints, returns the C return code."""
+    return int(load().fa_forward_fp8(Q8, Qs, K8, Ks, V8, Vs, O, LSE, B, H, N, d, float(scale),
+                                     int(causal), stream))
 
 
 def fa_backward_workspace_bytes(B, H, N, d, dtype) -> int:

@@ -169,6 +169,54 @@ def backward_dropout(q, k, v, o, do, lse, scale: float, causal: bool, p_drop: fl
     return dq, dk, dv
 
 
+def quantize_fp8(x, keys: bool = False):
+    """E4M3 codes and block exponent bytes (uint8 device tensors) of a bfloat16 [B, H, N, d] tensor.
+
+    keys=False (Q, K): codes [B, H, N, d], exponents [B, H, Np, d/32] (rows >= N: padding).
+    keys=True (V): codes [B, H, d, Np] (transposed, keys padded to Np = 64 * ceil(N/64)),
+    exponents [B, H, Np/32, d].
+    """
+    _check("x", x)
+    B, H, N, d, dt = _dims(x)
+    if dt != _lib.FA_BF16:
+        raise ValueError("fa_quantize_fp8 takes bfloat16 input")
+    layout = _lib.FA_FP8_KEYS if keys else _lib.FA_FP8_ROWS
+    Np = -(-N // 64) * 64
+    shape8 = (B, H, d, Np) if keys else (B, H, N, d)
+    shapes = (B, H, Np // 32, d) if keys else (B, H, Np, d // 32)
+    x8 = torch.empty(shape8, dtype=torch.uint8, device=x.device)
+    xs = torch.empty(shapes, dtype=torch.uint8, device=x.device)
+    assert x8.numel() == _lib.fa_fp8_bytes(B, H, N, d, layout)
+    assert xs.numel() == _lib.fa_fp8_scale_bytes(B, H, N, d, layout)
+    rc = _lib.fa_quantize_fp8(x.data_ptr(), x8.data_ptr(), xs.data_ptr(), B, H, N, d, layout,
+                              _stream(x.device))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_quantize_fp8")
+    return x8, xs
+
+
+def forward_fp8(q8, qs, k8, ks, v8, vs, scale: float, causal: bool = False):
+    """FP8 forward from ``quantize_fp8`` outputs: (O bfloat16, LSE float32)."""
+    B, H, N, d = q8.shape
+    for name, t in (("q8", q8), ("qs", qs), ("k8", k8), ("ks", ks), ("v8", v8), ("vs", vs)):
+        _check(name, t)
+        if t.dtype != torch.uint8:
+            raise ValueError(f"{name} must be uint8")
+    Np = -(-N // 64) * 64
+    if k8.shape != q8.shape or qs.shape != (B, H, Np, d // 32) or ks.shape != qs.shape:
+        raise ValueError("q8/k8 must be [B, H, N, d] with scales [B, H, Np, d/32]")
+    if v8.shape != (B, H, d, Np) or vs.shape != (B, H, Np // 32, d):
+        raise ValueError("v8 must be [B, H, d, Np] with scales [B, H, Np/32, d]")
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    rc = _lib.fa_forward_fp8(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(),
+                             v8.data_ptr(), vs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                             scale, int(bool(causal)), _stream(q8.device))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_forward_fp8")
+    return o, lse
+
+
 def workspace_bytes(B, H, N, d, dtype) -> int:
     return _lib.fa_backward_workspace_bytes(B, H, N, d, _DTYPES[dtype])
 

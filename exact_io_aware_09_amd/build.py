@@ -17,7 +17,7 @@ REPO_DIR = PKG_DIR.parent
 CSRC = PKG_DIR / "csrc"
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = PKG_DIR / LIB_NAME
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_f32.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_f32.hip"]
 ARCH = "gfx950"
 
 

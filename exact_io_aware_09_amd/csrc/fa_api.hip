@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 400;  // 0.4.0
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -211,6 +211,44 @@ int fa_backward_dropout(const void* Q, const void* K, const void* V, const void*
   hipError_t e = fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV,
                                           static_cast<float*>(workspace), p, fa::kStagesGrad,
                                           reinterpret_cast<hipStream_t>(stream), fa::SparseArgs{}, &dr);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+size_t fa_fp8_bytes(int B, int H, int N, int d, int layout) {
+  if (check_sizes(B, H, N, d, FA_BF16) != FA_OK) return 0;
+  if (layout == FA_FP8_ROWS) return (size_t)B * H * N * d;
+  if (layout == FA_FP8_KEYS) return (size_t)B * H * d * fa::fp8_keys_padded(N);
+  return 0;
+}
+size_t fa_fp8_scale_bytes(int B, int H, int N, int d, int layout) {
+  if (check_sizes(B, H, N, d, FA_BF16) != FA_OK) return 0;
+  if (layout == FA_FP8_ROWS) return (size_t)B * H * fa::fp8_keys_padded(N) * (d / 32);
+  if (layout == FA_FP8_KEYS) return (size_t)B * H * (fa::fp8_keys_padded(N) / 32) * d;
+  return 0;
+}
+int fa_quantize_fp8(const void* X, void* X8, void* Xs, int B, int H, int N, int d, int layout,
+                    void* stream) {
+  int rc = check_sizes(B, H, N, d, FA_BF16);
+  if (rc != FA_OK) return rc;
+  if (layout != FA_FP8_ROWS && layout != FA_FP8_KEYS) return FA_ERR_INVALID_ARG;
+  if (!X || !X8 || !Xs) return FA_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(X8) || !aligned16(Xs)) return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, 1.0f, false};
+  hipError_t e = fa::launch_quantize_fp8(X, X8, Xs, p, layout == FA_FP8_KEYS,
+                                         reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+int fa_forward_fp8(const void* Q8, const void* Qs, const void* K8, const void* Ks, const void* V8,
+                   const void* Vs, void* O, float* LSE, int B, int H, int N, int d, float scale,
+                   int causal, void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, FA_BF16);
+  if (rc != FA_OK) return rc;
+  if (!Q8 || !Qs || !K8 || !Ks || !V8 || !Vs || !O || !LSE) return FA_ERR_INVALID_ARG;
+  if (!aligned16(Q8) || !aligned16(Qs) || !aligned16(K8) || !aligned16(Ks) || !aligned16(V8) ||
+      !aligned16(Vs) || !aligned16(O) || !aligned16(LSE))
+    return FA_ERR_MISALIGNED;
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  hipError_t e = fa::launch_forward_fp8(Q8, Qs, K8, Ks, V8, Vs, O, LSE, p,
+                                        reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d, int dtype) {

@@ -72,6 +72,17 @@ hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, con
                                 float* Dws, const Problem& p, unsigned stages, hipStream_t stream,
                                 SparseArgs sp = {}, const DropArgs* dr = nullptr);
 
+// FP8 (E4M3) with power-of-two block scales.  Q and K: [B,H,N,d] bytes and
+// [B,H,Np,d/32] scale bytes (blocks of 32 head dims; rows padded to
+// Np = fp8_keys_padded(N)).  V: transposed [B,H,d,Np] bytes, keys padded
+// with zeros, and [B,H,Np/32,d] scale bytes (blocks of 32 keys).
+inline int fp8_keys_padded(int N) { return (N + 63) / 64 * 64; }
+hipError_t launch_quantize_fp8(const void* X, void* X8, void* Xs, const Problem& p, bool keys,
+                               hipStream_t stream);
+hipError_t launch_forward_fp8(const void* Q8, const void* Qs, const void* K8, const void* Ks,
+                              const void* V8, const void* Vs, void* O, float* LSE,
+                              const Problem& p, hipStream_t stream);
+
 // float32 throughout (vector ALU).
 hipError_t launch_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
                               const Problem& p, hipStream_t stream);

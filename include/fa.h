@@ -195,6 +195,54 @@ int fa_backward_dropout(const void* Q, const void* K, const void* V, const void*
                         void* stream);
 
 /*
+ * Attention forward in 8-bit floating point with block quantisation (the FP8
+ * variant of the third version of the kernel: CS324 notes, section 8.1;
+ * "FlashAttention and GPU memory", section 11).
+ *
+ * Format: OCP E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * largest finite 448), round to nearest even.  Every block of 32 elements
+ * along a contraction axis shares a power-of-two scale 2^e, stored as the
+ * byte e + 127; e is the smallest integer with max|x| <= 448 * 2^e (0 for an
+ * all-zero block), so an element x is stored as E4M3(x / 2^e) and never
+ * overflows.
+ *
+ * fa_quantize_fp8 converts a bfloat16 [B,H,N,d] tensor:
+ *   layout FA_FP8_ROWS (Q and K): X8 [B,H,N,d] bytes, Xs [B,H,Np,d/32]; block
+ *     = 32 consecutive head dims of a row (rows N .. Np-1 of Xs, padding,
+ *     hold 127: the exponent of an all-zero block).
+ *   layout FA_FP8_KEYS (V): X8 [B,H,d,Np] bytes (V transposed: keys
+ *     contiguous, padding 0), Xs [B,H,Np/32,d]; block = 32 consecutive keys
+ *     of one head dim.
+ * Np = N rounded up to a multiple of 64.
+ * fa_fp8_bytes / fa_fp8_scale_bytes give the sizes of X8 and Xs (0 for
+ * invalid sizes or layout).
+ *
+ * fa_forward_fp8 computes O (bfloat16 [B,H,N,d]) and LSE (float32 [B,H,N])
+ * of attention over the dequantised Q, K, V (Q and K in FA_FP8_ROWS, V in
+ * FA_FP8_KEYS): S = scale Q K^T with the scales applied by the matrix
+ * instructions, fp32 accumulation, the online softmax in fp32, and the
+ * weights rounded to E4M3 (times 2^8) for the product with V.  Relative to
+ * attention of the dequantised inputs, O differs by at most the E4M3
+ * rounding of the weights (2^-4 relative, 2^-18 absolute per weight) plus the
+ * bfloat16 rounding of O.
+ *
+ * All pointers 16-byte aligned device memory; other arguments and errors as
+ * fa_forward (inputs are bfloat16 for fa_quantize_fp8).
+ */
+enum { FA_FP8_ROWS = 0, FA_FP8_KEYS = 1 };
+
+size_t fa_fp8_bytes(int B, int H, int N, int d, int layout);
+
+size_t fa_fp8_scale_bytes(int B, int H, int N, int d, int layout);
+
+int fa_quantize_fp8(const void* X, void* X8, void* Xs, int B, int H, int N, int d, int layout,
+                    void* stream);
+
+int fa_forward_fp8(const void* Q8, const void* Qs, const void* K8, const void* Ks, const void* V8,
+                   const void* Vs, void* O, float* LSE, int B, int H, int N, int d, float scale,
+                   int causal, void* stream);
+
+/*
  * Bytes of device workspace fa_backward needs: two float32 vectors of one
  * value per query row (B*H*N rows), each starting on a 256-byte boundary --
  * -D_i = -sum_k dO_ik O_ik (D is the vector of CS324 notes section 5.4;

@@ -178,3 +178,40 @@ def test_backward_dropout_validation(args, code):
               seed=7, dtype=_lib.FA_BF16, stream=None)
     kw.update(args)
     assert fa.fa_backward_dropout(**kw) == code
+
+
+def test_fp8_sizes():
+    assert fa.fa_fp8_bytes(2, 3, 100, 64, _lib.FA_FP8_ROWS) == 2 * 3 * 100 * 64
+    assert fa.fa_fp8_scale_bytes(2, 3, 100, 64, _lib.FA_FP8_ROWS) == 2 * 3 * 128 * 2    # rows padded to 128
+    assert fa.fa_fp8_bytes(2, 3, 100, 64, _lib.FA_FP8_KEYS) == 2 * 3 * 64 * 128     # keys padded to 128
+    assert fa.fa_fp8_scale_bytes(2, 3, 100, 64, _lib.FA_FP8_KEYS) == 2 * 3 * 4 * 64
+    assert fa.fa_fp8_bytes(2, 3, 100, 64, 2) == 0
+    assert fa.fa_fp8_bytes(2, 3, 100, 80, _lib.FA_FP8_ROWS) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(layout=2), _lib.FA_ERR_INVALID_ARG),
+    (dict(X=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(Xs=A + 1), _lib.FA_ERR_MISALIGNED),
+    (dict(d=32), _lib.FA_ERR_UNSUPPORTED),
+    (dict(N=0), _lib.FA_ERR_INVALID_ARG),
+])
+def test_quantize_fp8_validation(args, code):
+    kw = dict(X=A, X8=A, Xs=A, B=1, H=1, N=64, d=64, layout=_lib.FA_FP8_ROWS, stream=None)
+    kw.update(args)
+    assert fa.fa_quantize_fp8(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(Ks=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(LSE=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(V8=A + 4), _lib.FA_ERR_MISALIGNED),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), _lib.FA_ERR_INVALID_ARG),
+    (dict(causal=5), _lib.FA_ERR_INVALID_ARG),
+])
+def test_forward_fp8_validation(args, code):
+    kw = dict(Q8=A, Qs=A, K8=A, Ks=A, V8=A, Vs=A, O=A, LSE=A, B=1, H=1, N=64, d=64, scale=0.125,
+              causal=0, stream=None)
+    kw.update(args)
+    assert fa.fa_forward_fp8(**kw) == code
