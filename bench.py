@@ -33,6 +33,7 @@ if str(ROOT) not in sys.path:
 
 METRIC = "attention fwd+bwd TFLOP/s & % bf16 MFMA peak (B64 H16 N1024 d64 causal)"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic.json"
 KERNELS = ("fwd", "bwd_dq", "bwd_dkdv")
@@ -55,6 +56,9 @@ def parse_args(argv=None):
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="drop probability of the fused dropout (fa_forward_dropout / "
                          "fa_backward_dropout); 0 = no dropout")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 forward (fa_forward_fp8) on inputs quantised beforehand "
+                         "with fa_quantize_fp8; implies --fwd-only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -266,6 +270,15 @@ def main(argv=None):
     if drop and (sparse or args.splits > 1):
         print("bench.py: --dropout runs the dense path only", file=sys.stderr)
         return 2
+    if args.fp8 and (drop or sparse or args.splits > 1 or dtype_name != "bf16"):
+        print("bench.py: --fp8 runs the dense bfloat16-input path only", file=sys.stderr)
+        return 2
+    if args.fp8:
+        args.fwd_only = True
+        q8, qs = fa.quantize_fp8(q)
+        k8, ks = fa.quantize_fp8(k)
+        v8, vs = fa.quantize_fp8(v, keys=True)
+        P8 = [t.data_ptr() for t in (q8, qs, k8, ks, v8, vs)]
     fused = sparse or drop  # one backward call: events around forward and backward only
     maskd = band_mask(N).to(dev) if sparse else None
     wsb = fa.workspace_bytes(B, H, N, d, w.dtype)
@@ -294,6 +307,11 @@ def main(argv=None):
                                          P[6], P[7], P[8], P[9], wsb, B, H, N, d, w.scale,
                                          int(w.causal), dt, sp), "fa_backward_sparse")
             rec(2)
+            return
+        if args.fp8:
+            call(_lib.fa_forward_fp8(*P8, P[3], P[4], B, H, N, d, w.scale, int(w.causal), sp),
+                 "fa_forward_fp8")
+            rec(1)
             return
         if drop:
             call(_lib.fa_forward_dropout(P[0], P[1], P[2], P[3], P[4], B, H, N, d, w.scale,
@@ -342,7 +360,7 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    names = (("fwd_split",) if args.splits > 1 else
+    names = (("fwd_split",) if args.splits > 1 else ("fwd_fp8",) if args.fp8 else
              ("fwd_sparse", "bwd_sparse")[: nev - 1] if sparse else
              ("fwd_dropout", "bwd_dropout")[: nev - 1] if drop else KERNELS[: nev - 1])
     per_kernel = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
@@ -360,6 +378,9 @@ def main(argv=None):
         # visible pair of the mask
         per = 2 if dom == "fwd_sparse" else 7
         bound, amount = "mfma", per * 2 * w.d * mask_pairs(w, band_mask(N))
+    elif args.fp8:
+        # the forward's two contractions per visible pair, at the fp8 peak
+        bound, amount = "mfma", 4 * w.d * visible_pairs(w)
     elif drop:
         # as above, per visible (query, key) pair of the causal or full pattern
         per = 2 if dom == "fwd_dropout" else 7
@@ -368,7 +389,8 @@ def main(argv=None):
         bound, amount, _ = algorithmic(w, dom, 2 if dtype_name == "bf16" else 4)
     dur_s = per_kernel[dom] * 1e-3
     if bound == "mfma":
-        achieved, peak, unit = amount / dur_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        achieved, unit = amount / dur_s / 1e12, "TFLOP/s"
+        peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     else:
         achieved, peak, unit = amount / dur_s / 1e9, PEAK_HBM_GBS, "GB/s"
 
@@ -377,7 +399,8 @@ def main(argv=None):
         else (f"attention {'fwd' if args.fwd_only else 'fwd+bwd'} TFLOP/s ({args.workload}"
               + (f", {args.splits} key ranges)" if args.splits > 1 else
                  ", block-sparse band tiles, FLOPs of visible pairs)" if sparse else
-                 f", dropout {args.dropout})" if drop else ")")),
+                 f", dropout {args.dropout})" if drop else
+                 ", FP8 E4M3 with block scales)" if args.fp8 else ")")),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -387,7 +410,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype_name,
+        "dtype": "fp8" if args.fp8 else dtype_name,
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                    "scale": w.scale, "input_dtype": dtype_name,
@@ -395,8 +418,10 @@ def main(argv=None):
                    **({"tile_mask": "band |I-J|<=2", "visible_pairs": mask_pairs(w, band_mask(N))}
                       if sparse else {}),
                    **({"splits": args.splits} if args.splits > 1 else {}),
-                   **({"dropout": args.dropout, "seed": DROPOUT_SEED} if drop else {})},
+                   **({"dropout": args.dropout, "seed": DROPOUT_SEED} if drop else {}),
+                   **({"fp8": "E4M3, power-of-two scale per 32 elements"} if args.fp8 else {})},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        **({"pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2)} if args.fp8 else {}),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "peak_mem_bytes": torch.cuda.max_memory_allocated(dev),
@@ -411,7 +436,7 @@ def main(argv=None):
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and not fused and args.splits == 1:
+    if not args.no_cpu_baseline and not fused and args.splits == 1 and not args.fp8:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
