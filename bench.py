@@ -67,13 +67,22 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
-def source_digest() -> str:
+# Translation unit of each timed kernel: its source file and the headers it includes.
+KERNEL_SOURCES = {
+    "fwd": ("fa_fwd.hip", "fa_device.h", "fa_dropout.h", "fa_launch.h"),
+    "bwd_dq": ("fa_bwd.hip", "fa_device.h", "fa_dropout.h", "fa_launch.h"),
+    "bwd_dkdv": ("fa_bwd.hip", "fa_device.h", "fa_dropout.h", "fa_launch.h"),
+    "bwd_pre": ("fa_bwd.hip", "fa_device.h", "fa_dropout.h", "fa_launch.h"),
+}
+
+
+def source_digest(kernel: str) -> str:
+    """sha256 over the sources a kernel is compiled from (counters go stale when they change)."""
     h = hashlib.sha256()
     csrc = ROOT / "exact_io_aware_09_amd" / "csrc"
-    for p in sorted(csrc.glob("*")):
-        if p.suffix in (".hip", ".h"):
-            h.update(p.name.encode())
-            h.update(p.read_bytes())
+    for name in KERNEL_SOURCES[kernel]:
+        h.update(name.encode())
+        h.update((csrc / name).read_bytes())
     return h.hexdigest()
 
 
@@ -146,10 +155,10 @@ def stored_traffic(kernel, workload):
         data = json.loads(TRAFFIC_FILE.read_text())
     except (OSError, ValueError):
         return None
-    if data.get("source_sha256") != source_digest() or data.get("workload") != workload:
+    if data.get("workload") != workload or kernel not in KERNEL_SOURCES:
         return None
     k = data.get("kernels", {}).get(kernel)
-    if not k:
+    if not k or k.get("source_sha256") != source_digest(kernel):
         return None
     return int(k["fetch_bytes"]) + int(k["write_bytes"])
 
