@@ -13,6 +13,7 @@
   causal GPT-2-medium shape.
 * p_drop = 0 reproduces fa_forward / fa_backward bit for bit.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -130,3 +131,41 @@ def test_same_seed_same_result_and_seed_matters():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert not torch.equal(a, c)
+
+
+def test_long_sequence_sampled_rows():
+    # N = 65,536 causal: counters reach query and key tiles up to 16,383; O, LSE
+    # and dQ of sampled query rows against the oracle (full rows, the mask drawn
+    # for exactly those rows)
+    from oracle.attention import scores, softmax_rows
+    from exact_io_aware_09_amd.workloads import WORKLOADS, sample_rows
+    w = WORKLOADS["long"]
+    B, H, N, d = w.shape
+    q, k, v, do = make_inputs(w.shape, torch.bfloat16, w.seed)
+    p, seed = 0.1, 0xFEEDFACE12345
+    o, lse, dq, dk, dv = run_dropout(q, k, v, do, w.scale, True, p, seed)
+    t = DR.keep_threshold(p)
+    for h in (0, H - 1):
+        rows = np.unique(np.concatenate([sample_rows(w.seed, 0, h, H, N, count=24)[0][:24], [N - 1]]))
+        qh, kh, vh, doh = (x[0, h].double() for x in (q, k, v, do))
+        s = w.scale * (qh[rows] @ kh.T)
+        s = s.masked_fill(torch.arange(N).unsqueeze(0) > torch.as_tensor(rows).unsqueeze(1), float("-inf"))
+        pr, m, l = softmax_rows(s)
+        z = torch.from_numpy(DR.draws(seed, h, rows, np.arange(N)) < t).double() * (256.0 / t)
+        ro = (pr * z) @ vh
+        rl = m + torch.log(l)
+        dp = (doh[rows] @ vh.T) * z
+        dd = (doh[rows] * ro).sum(-1, keepdim=True)
+        rdq = w.scale * ((pr * (dp - dd)) @ kh)
+        assert max_abs(o[0, h][rows], ro) <= 2e-2 * 256 / t, f"head {h}: O"
+        assert max_abs(lse[0, h][rows], rl) <= 1e-3, f"head {h}: LSE"
+        assert rel_frob(dq[0, h][rows], rdq) <= 5e-2, f"head {h}: dQ relF {rel_frob(dq[0, h][rows], rdq)}"
+
+
+def test_dropout_bitwise_deterministic():
+    shape = (2, 3, 333, 128)
+    q, k, v, do = make_inputs(shape, torch.bfloat16, 12)
+    a = run_dropout(q, k, v, do, 0.1, True, 0.3, 99)
+    b = run_dropout(q, k, v, do, 0.1, True, 0.3, 99)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -126,3 +126,23 @@ def test_forward_fp8_workload_shapes(name):
         rows = np.arange(N) if N <= 1024 else sample_rows(w.seed, b, h, H, N)[0]
         check_head(o[b, h][rows], lse[b, h][rows], q[b, h], k[b, h], v[b, h], w.scale, w.causal, rows,
                    f"{name} head ({b},{h})")
+
+
+def test_forward_fp8_long_causal_sampled():
+    # N = 65,536, causal: 1,024 key blocks per row; sampled rows of two heads
+    w = WORKLOADS["long"]
+    B, H, N, d = w.shape
+    q, k, v = make_inputs(w.shape, torch.bfloat16, w.seed)[:3]
+    o, lse = run_fp8(q, k, v, w.scale, True)
+    for h in (0, H - 1):
+        rows = np.unique(np.concatenate([sample_rows(w.seed, 0, h, H, N, count=32)[0][:32], [0, N - 1]]))
+        check_head(o[0, h][rows], lse[0, h][rows], q[0, h], k[0, h], v[0, h], w.scale, True, rows,
+                   f"long head {h}")
+
+
+def test_forward_fp8_bitwise_deterministic():
+    shape = (2, 2, 300, 128)
+    q, k, v = make_inputs(shape, torch.bfloat16, 14)[:3]
+    a = run_fp8(q, k, v, 0.1, True)
+    b = run_fp8(q, k, v, 0.1, True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
