@@ -12,6 +12,7 @@ from ._lib import (FA_BF16, FA_F32, FA_FP8_KEYS, FA_FP8_ROWS, FAError,  # noqa: 
                    fa_forward_sparse, fa_forward_split, fa_fp8_bytes, fa_fp8_scale_bytes,
                    fa_quantize_fp8,
                    fa_forward_split_workspace_bytes, fa_merge_partials, fa_strerror, fa_version)
+from .autograd import FlashAttentionFunction, flash_attention  # noqa: F401
 from .attention import (backward, backward_dropout, backward_sparse, forward,  # noqa: F401
                         forward_dropout, forward_fp8, forward_sparse, forward_split,
                         merge_partials, quantize_fp8, workspace_bytes)
@@ -24,4 +25,5 @@ __all__ = [
     "forward_sparse", "backward_sparse", "fa_forward_dropout", "fa_backward_dropout",
     "forward_dropout", "backward_dropout", "FA_FP8_ROWS", "FA_FP8_KEYS", "fa_fp8_bytes",
     "fa_fp8_scale_bytes", "fa_quantize_fp8", "fa_forward_fp8", "quantize_fp8", "forward_fp8",
+    "flash_attention", "FlashAttentionFunction",
 ]
