@@ -43,7 +43,7 @@ DROPOUT_SEED = 0x5EED0F00D
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2_medium")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward kernel")
@@ -163,6 +163,17 @@ def stored_traffic(kernel, workload):
     return int(k["fetch_bytes"]) + int(k["write_bytes"])
 
 
+def host_cpu() -> str:
+    """CPU model of the host (first 'model name' of /proc/cpuinfo)."""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_sampled(w, seconds: float):
     """Time the sampled-row oracle on query rows of the first head (N too large for S)."""
     import torch
@@ -186,6 +197,7 @@ def cpu_baseline_sampled(w, seconds: float):
         "value": tflops,
         "unit": "TFLOP/s",
         "cores": torch.get_num_threads(),
+        "cpu_model": host_cpu(),
         "kind": "oracle",
         "sample": (f"fp64 sampled-row oracle (full score rows, O, LSE and dQ per row) on {done} "
                    f"query rows of head 0 of the {w.name} workload (N={w.N}, d={w.d}, "
@@ -222,6 +234,7 @@ def cpu_baseline(w, seconds: float):
         "value": tflops,
         "unit": "TFLOP/s",
         "cores": torch.get_num_threads(),
+        "cpu_model": host_cpu(),
         "kind": "oracle",
         "sample": (f"fp64 oracle forward+backward (S, P materialised) on {heads_done} heads "
                    f"(N={w.N}, d={w.d}, causal={w.causal}) of the {w.name} workload's "
@@ -374,6 +387,7 @@ def main(argv=None):
              ("fwd_dropout", "bwd_dropout")[: nev - 1] if drop else KERNELS[: nev - 1])
     per_kernel = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                   for i, n in enumerate(names)}
+    step_ms = sorted(e[0].elapsed_time(e[-1]) for e in evs)
 
     fwd_fl, bwd_fl = credited_flops(w)
     if sparse:
@@ -433,6 +447,8 @@ def main(argv=None):
         **({"pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2)} if args.fp8 else {}),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "step_ms_median": round(step_ms[len(step_ms) // 2], 4),
+        "step_ms_min": round(step_ms[0], 4),
         "peak_mem_bytes": torch.cuda.max_memory_allocated(dev),
         "roofline": {
             "kernel": dom,
