@@ -46,12 +46,14 @@ def run_dropout(q, k, v, do, scale, causal, p, seed):
     return tuple(t.cpu() for t in (o, lse, dq, dk, dv))
 
 
+@pytest.mark.parametrize("p", [0.3, 0.998])
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
-def test_masks_are_the_oracle_draws(d, causal):
-    # N = d so that V = I and dO = I read the masks out; B*H = 6 heads
+def test_masks_are_the_oracle_draws(d, causal, p):
+    # N = d so that V = I and dO = I read the masks out; B*H = 6 heads.
+    # p = 0.998 is the largest p with t >= 1 (one draw value in 256 kept).
     B, H, N = 2, 3, d
-    p, seed = 0.3, 0x0123456789ABCDEF
+    seed = 0x0123456789ABCDEF
     t = DR.keep_threshold(p)
     eye = torch.eye(N, dtype=torch.bfloat16).expand(B, H, N, N).contiguous()
     zero = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
@@ -169,3 +171,19 @@ def test_dropout_bitwise_deterministic():
     b = run_dropout(q, k, v, do, 0.1, True, 0.3, 99)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("N", [31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257])
+def test_dropout_tile_boundaries(N):
+    # sequence lengths around the 32-key blocks, 128-row workgroups and the
+    # 4 x 4 draw tiles; causal, d = 64
+    shape = (1, 2, N, 64)
+    q, k, v, do = make_inputs(shape, torch.bfloat16, 100 + N)
+    p, seed = 0.25, 555 + N
+    o, lse, dq, dk, dv = run_dropout(q, k, v, do, 0.125, True, p, seed)
+    t = DR.keep_threshold(p)
+    keep = DR.keep_masks(seed, 1, 2, N, t)
+    ro, rl, rdq, rdk, rdv = DR.attention_forward_backward_dropout(q, k, v, do, 0.125, True, keep, t)
+    assert max_abs(o, ro) <= 2e-2 * 256 / t and max_abs(lse, rl) <= 1e-3, f"N={N}"
+    for name, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert rel_frob(g, r) <= 5e-2, f"N={N}: {name} relF {rel_frob(g, r)}"

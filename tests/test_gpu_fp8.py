@@ -146,3 +146,13 @@ def test_forward_fp8_bitwise_deterministic():
     a = run_fp8(q, k, v, 0.1, True)
     b = run_fp8(q, k, v, 0.1, True)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("N", [31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257])
+def test_forward_fp8_tile_boundaries(N):
+    # sequence lengths around the 64-key blocks, the 128-row workgroups and
+    # the 32-element scale blocks of V; causal, d = 128
+    shape = (1, 1, N, 128)
+    q, k, v = make_inputs(shape, torch.bfloat16, 200 + N)[:3]
+    o, lse = run_fp8(q, k, v, 128 ** -0.5, True)
+    check_head(o[0, 0], lse[0, 0], q[0, 0], k[0, 0], v[0, 0], 128 ** -0.5, True, np.arange(N), f"N={N}")
