@@ -113,33 +113,51 @@ void quant_rows_kernel(const bf16_t* __restrict__ X, uint8_t* __restrict__ X8,
   Xs[b] = (uint8_t)eb;
 }
 
-// V: one thread per (head, block of 32 keys, head dim), head dim fastest
-// (coalesced reads of each key row); writes V^T [D, Np] rows and the scale
-// of the block at Vs[(head * Np/32 + block) * D + dim].  Keys >= N are 0.
+// V: one workgroup per (head, 64 keys), staged through LDS so that both the
+// bfloat16 rows read and the transposed E4M3 rows written are coalesced.
+// Each thread quantises (head dim, 32-key block) items from the LDS copy;
+// the codes go to an LDS tile [D][64] that is then written out as whole
+// 64-byte rows of V^T [D, Np], the scale of block kb to
+// Vs[(head * Np/32 + kb) * D + dim].  Keys >= N are 0.
 template <int D>
 __global__ __launch_bounds__(256)
 void quant_keys_kernel(const bf16_t* __restrict__ V, uint8_t* __restrict__ V8,
-                       uint8_t* __restrict__ Vs, long long total, int N, int Np) {
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= total) return;
-  const int nkb = Np / 32;
-  const int d = (int)(t % D);
-  const long long r = t / D;
-  const int kb = (int)(r % nkb);
-  const long long bh = r / nkb;
-  const bf16_t* src = V + (size_t)bh * N * D + d;
-  float v[32];
+                       uint8_t* __restrict__ Vs, int N, int Np) {
+  __shared__ __attribute__((aligned(16))) bf16_t vin[64 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t vout[D * 64];
+  const int tid = threadIdx.x;
+  const int tiles = Np / 64;
+  const long long bh = blockIdx.x / tiles;
+  const int j0 = (blockIdx.x % tiles) * 64;
+  const bf16_t* src = V + (size_t)bh * N * D;
+  constexpr int CPR = D / 8;  // 16-byte chunks per key row
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int key = kb * 32 + i;
-    v[i] = key < N ? bf16_to_f32(src[(size_t)key * D]) : 0.f;
+  for (int i = tid; i < 64 * CPR; i += 256) {
+    const int r = i / CPR, cc = i % CPR;
+    const uint4 u = j0 + r < N ? *reinterpret_cast<const uint4*>(src + (size_t)(j0 + r) * D + cc * 8)
+                               : make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(vin + r * D + cc * 8) = u;
   }
-  uint32_t q[8];
-  const uint32_t eb = quantize32(v, q);
-  uint4* dst = reinterpret_cast<uint4*>(V8 + ((size_t)bh * D + d) * Np + kb * 32);
-  dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
-  dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
-  Vs[((size_t)bh * nkb + kb) * D + d] = (uint8_t)eb;
+  __syncthreads();
+  for (int it = tid; it < 2 * D; it += 256) {
+    const int d = it % D, kb = it / D;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(vin[(32 * kb + i) * D + d]);
+    uint32_t q[8];
+    const uint32_t eb = quantize32(v, q);
+    uint4* dst = reinterpret_cast<uint4*>(vout + d * 64 + 32 * kb);
+    dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+    dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+    Vs[((size_t)bh * (Np / 32) + j0 / 32 + kb) * D + d] = (uint8_t)eb;
+  }
+  __syncthreads();
+  uint8_t* out = V8 + (size_t)bh * D * Np + j0;
+  for (int i = tid; i < D * 4; i += 256) {
+    const int d = i / 4, cc = i % 4;
+    *reinterpret_cast<uint4*>(out + (size_t)d * Np + cc * 16) =
+        *reinterpret_cast<const uint4*>(vout + d * 64 + cc * 16);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -476,21 +494,20 @@ hipError_t launch_quantize_fp8(const void* X, void* X8, void* Xs, const Problem&
     }
     return hipGetLastError();
   }
-  const long long total = BH * (Np / 32) * p.d;
-  const long long grid = (total + 255) / 256;
+  const long long grid = BH * (Np / 64);
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   switch (p.d) {
     case 64:
       hipLaunchKernelGGL(quant_keys_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream,
-                         (const bf16_t*)X, (uint8_t*)X8, (uint8_t*)Xs, total, p.N, Np);
+                         (const bf16_t*)X, (uint8_t*)X8, (uint8_t*)Xs, p.N, Np);
       break;
     case 128:
       hipLaunchKernelGGL(quant_keys_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream,
-                         (const bf16_t*)X, (uint8_t*)X8, (uint8_t*)Xs, total, p.N, Np);
+                         (const bf16_t*)X, (uint8_t*)X8, (uint8_t*)Xs, p.N, Np);
       break;
     case 256:
       hipLaunchKernelGGL(quant_keys_kernel<256>, dim3((unsigned)grid), dim3(256), 0, stream,
-                         (const bf16_t*)X, (uint8_t*)X8, (uint8_t*)Xs, total, p.N, Np);
+                         (const bf16_t*)X, (uint8_t*)X8, (uint8_t*)Xs, p.N, Np);
       break;
     default:
       return hipErrorInvalidValue;
