@@ -875,7 +875,7 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
 #define FA_BWD_CFG_D64 4, 1, 1, 2, 2, 4, 1, 32, 2, 3
 #endif
 #ifndef FA_BWD_CFG_D128
-#define FA_BWD_CFG_D128 4, 1, 1, 2, 1, 4, 1, 64, 2, 1
+#define FA_BWD_CFG_D128 4, 1, 1, 2, 1, 4, 1, 32, 2, 2
 #endif
 #ifndef FA_BWD_CFG_D256
 #define FA_BWD_CFG_D256 4, 1, 1, 2, 1, 4, 1, 32, 2, 1
