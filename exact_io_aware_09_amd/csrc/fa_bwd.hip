@@ -107,8 +107,13 @@ struct DkdvCfg {
 // - D) computed as (256/t) P (Z ? dP' - D t/256 : -D t/256) by starting the
 // dP' accumulation from -D t/256; the factor 256/t of dK is part of `scale`
 // (the host passes scale * 256/t).
+//
+// PARTS: bit 0 = dV, bit 1 = dK.  A launch with one part recomputes S (and,
+// for dK, dP) and accumulates only that gradient: two launches instead of
+// one when the two accumulators would not fit the registers (head dim 256:
+// 2 x 128 registers of accumulators beside 128 of K and V fragments).
 template <int D, int NW, int KB, int QB, int ST, int OCC, bool CAUSAL, bool SPARSE = false,
-          bool DROP = false>
+          bool DROP = false, int PARTS = 3>
 __global__ __launch_bounds__(NW * 64, OCC)
 void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                           const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
@@ -119,6 +124,8 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   using C = DkdvCfg<D, NW, KB, QB, ST>;
   static_assert(!(SPARSE && DROP), "one variant at a time");
   static_assert(!SPARSE || (ST == 2 && C::BK == 128), "sparse walk: two stages, 128-key blocks");
+  static_assert(PARTS >= 1 && PARTS <= 3, "dV, dK or both");
+  constexpr bool DVP = PARTS & 1, DKP = PARTS & 2;
   // per stage: Q tile, dO tile, and 64 floats each of LSE*log2e and D
   __shared__ __attribute__((aligned(16))) bf16_t q0s[C::TILE], o0s[C::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t q1s[C::TILE], o1s[C::TILE];
@@ -203,7 +210,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       for (int s = 0; s < C::KSTEPS; ++s) {
         const uint32_t off = ((uint32_t)(k0w + 32 * kk + c32) * D + 16 * s + 8 * h) * 2u;
         kf[kk][s] = as_bf16x8(buf_load16(rk, off));
-        vf[kk][s] = as_bf16x8(buf_load16(rv, off));
+        if constexpr (DKP) vf[kk][s] = as_bf16x8(buf_load16(rv, off));
       }
     // K and V resident here: the compiler does not count the copies, so its
     // own waits for K and V must not fall inside the loop (where they would
@@ -213,7 +220,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         pin_ready(kf[kk][s]);
-        pin_ready(vf[kk][s]);
+        if constexpr (DKP) pin_ready(vf[kk][s]);
       }
   }
   if constexpr (ST > 2) {
@@ -228,7 +235,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         kf[kk][s] = frag_rows<D>(ksg, w * C::KW + 32 * kk, 16 * s, c32, h);
-        vf[kk][s] = frag_rows<D>(vsg, w * C::KW + 32 * kk, 16 * s, c32, h);
+        if constexpr (DKP) vf[kk][s] = frag_rows<D>(vsg, w * C::KW + 32 * kk, 16 * s, c32, h);
       }
   }
 
@@ -256,28 +263,29 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       f32x16 ndq[DROP ? QB : 1];  // DROP: -D t/256, the dS factor of dropped pairs
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        f32x16 nd;
+        f32x16 nd = {};
+        if constexpr (DKP) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(ds + qb * 32 + 8 * g + 4 * h);
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(ds + qb * 32 + 8 * g + 4 * h);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) nd[4 * g + e] = DROP ? v[e] * dr.keep : v[e];
+            for (int e = 0; e < 4; ++e) nd[4 * g + e] = DROP ? v[e] * dr.keep : v[e];
+          }
         }
         if constexpr (DROP) ndq[qb] = nd;
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
           const bf16x8 aq = frag_rows<D>(Qs, qb * 32, 16 * s, c32, h);
-          const bf16x8 ao = frag_rows<D>(Os, qb * 32, 16 * s, c32, h);
 #pragma unroll
           for (int kk = 0; kk < KB; ++kk) {
-            if (s == 0) {
-              const f32x16 z = {};
-              sacc[qb][kk] = mfma32x32x16(aq, kf[kk][s], z);
-              pacc[qb][kk] = mfma32x32x16(ao, vf[kk][s], nd);
-            } else {
-              sacc[qb][kk] = mfma32x32x16(aq, kf[kk][s], sacc[qb][kk]);
-              pacc[qb][kk] = mfma32x32x16(ao, vf[kk][s], pacc[qb][kk]);
-            }
+            const f32x16 z = {};
+            sacc[qb][kk] = mfma32x32x16(aq, kf[kk][s], s == 0 ? z : sacc[qb][kk]);
+          }
+          if constexpr (DKP) {
+            const bf16x8 ao = frag_rows<D>(Os, qb * 32, 16 * s, c32, h);
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+              pacc[qb][kk] = mfma32x32x16(ao, vf[kk][s], s == 0 ? nd : pacc[qb][kk]);
           }
         }
       }
@@ -339,7 +347,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
             for (int r = 0; r < 16; ++r) {
               const bool k = kept(dw, r, dr.thresh);
               const float pv = sacc[qb][kk][r];
-              pacc[qb][kk][r] = pv * (k ? pacc[qb][kk][r] : ndq[qb][r]);
+              if constexpr (DKP) pacc[qb][kk][r] = pv * (k ? pacc[qb][kk][r] : ndq[qb][r]);
               sacc[qb][kk][r] = k ? pv : 0.f;
             }
           }
@@ -352,15 +360,19 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x16& pr = sacc[qb][kk];
-            float dsv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              dsv[e] = DROP ? pacc[qb][kk][4 * g + e] : pr[4 * g + e] * pacc[qb][kk][4 * g + e];
             const int u = 2 * qb + (g >> 1), w0 = 2 * (g & 1);
-            pw[kk][u][w0] = pack_bf16x2(pr[4 * g], pr[4 * g + 1]);
-            pw[kk][u][w0 + 1] = pack_bf16x2(pr[4 * g + 2], pr[4 * g + 3]);
-            sw[kk][u][w0] = pack_bf16x2(dsv[0], dsv[1]);
-            sw[kk][u][w0 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+            if constexpr (DVP) {
+              pw[kk][u][w0] = pack_bf16x2(pr[4 * g], pr[4 * g + 1]);
+              pw[kk][u][w0 + 1] = pack_bf16x2(pr[4 * g + 2], pr[4 * g + 3]);
+            }
+            if constexpr (DKP) {
+              float dsv[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                dsv[e] = DROP ? pacc[qb][kk][4 * g + e] : pr[4 * g + e] * pacc[qb][kk][4 * g + e];
+              sw[kk][u][w0] = pack_bf16x2(dsv[0], dsv[1]);
+              sw[kk][u][w0 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+            }
           }
 
       // dV^T += dO^T P,  dK^T += Q^T dS  (lane: key; registers: head dims);
@@ -369,14 +381,19 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
       for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
         for (int u = 0; u < C::PU; ++u) {
-          const bf16x8 ao = frag_tr<D>(Os, 16 * u, db * 32, lane);
-          const bf16x8 aq = frag_tr<D>(Qs, 16 * u, db * 32, lane);
+          if constexpr (DVP) {
+            const bf16x8 ao = frag_tr<D>(Os, 16 * u, db * 32, lane);
 #pragma unroll
-          for (int kk = 0; kk < KB; ++kk) {
-            dvacc[kk][db] = mfma32x32x16(
-                ao, bf16x8_from(pw[kk][u][0], pw[kk][u][1], pw[kk][u][2], pw[kk][u][3]), dvacc[kk][db]);
-            dkacc[kk][db] = mfma32x32x16(
-                aq, bf16x8_from(sw[kk][u][0], sw[kk][u][1], sw[kk][u][2], sw[kk][u][3]), dkacc[kk][db]);
+            for (int kk = 0; kk < KB; ++kk)
+              dvacc[kk][db] = mfma32x32x16(
+                  ao, bf16x8_from(pw[kk][u][0], pw[kk][u][1], pw[kk][u][2], pw[kk][u][3]), dvacc[kk][db]);
+          }
+          if constexpr (DKP) {
+            const bf16x8 aq = frag_tr<D>(Qs, 16 * u, db * 32, lane);
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+              dkacc[kk][db] = mfma32x32x16(
+                  aq, bf16x8_from(sw[kk][u][0], sw[kk][u][1], sw[kk][u][2], sw[kk][u][3]), dkacc[kk][db]);
           }
         }
       }
@@ -408,7 +425,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     }
   }
 
-  if constexpr (DROP) {
+  if constexpr (DROP && DVP) {
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
@@ -421,6 +438,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     // this wavefront's rows of the staging tiles, then out as whole rows:
     // 8 lanes per row, each store instruction writes 8 complete rows
     constexpr int CPR = D / 8;
+    static_assert(PARTS == 3, "LDS-staged K/V: both gradients in one launch");
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
@@ -471,8 +489,8 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
               vv[e] = to_bf16(dvacc[kk][db][4 * g + e]);
             }
             const int col = db * 32 + 8 * g + 4 * h;
-            *reinterpret_cast<bf16x4*>(dKr + col) = vk;
-            *reinterpret_cast<bf16x4*>(dVr + col) = vv;
+            if constexpr (DKP) *reinterpret_cast<bf16x4*>(dKr + col) = vk;
+            if constexpr (DVP) *reinterpret_cast<bf16x4*>(dVr + col) = vv;
           }
       }
     }
@@ -817,6 +835,13 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
   }
 }
 
+// Head dims whose dK and dV are accumulated by two launches (dV, then dK).
+#ifndef FA_DKDV_SPLIT_D256
+#define FA_DKDV_SPLIT_D256 true
+#endif
+template <int D>
+constexpr bool kDkdvSplit = D == 256 ? FA_DKDV_SPLIT_D256 : false;
+
 template <int D, int NWK, int KBK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ,
           int OCCQ, bool CAUSAL, bool SPARSE, bool DROP = false>
 hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -856,12 +881,24 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
     const long long grid = (long long)BH * nkb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int G = head_group(OCCK * 4 / NWK, nkb);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, KBK, QB, STK, OCCK, CAUSAL, SPARSE, DROP>),
-                       dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
-                       (const bf16_t*)V, (const bf16_t*)dO, (const float*)Lws, (const float*)Dws,
-                       (bf16_t*)dK, (bf16_t*)dV, BH, p.N, nkb, G, c, gscale, sp, dr);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    auto launch = [&](auto parts) {
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWK, KBK, QB, STK, OCCK, CAUSAL, SPARSE, DROP,
+                                               decltype(parts)::value>),
+                         dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q,
+                         (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)dO, (const float*)Lws,
+                         (const float*)Dws, (bf16_t*)dK, (bf16_t*)dV, BH, p.N, nkb, G, c, gscale,
+                         sp, dr);
+      return hipGetLastError();
+    };
+    if constexpr (kDkdvSplit<D>) {
+      hipError_t e = launch(std::integral_constant<int, 1>{});  // dV
+      if (e != hipSuccess) return e;
+      e = launch(std::integral_constant<int, 2>{});             // dK
+      if (e != hipSuccess) return e;
+    } else {
+      hipError_t e = launch(std::integral_constant<int, 3>{});
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
