@@ -53,8 +53,10 @@ def rocrand_philox(tmp_path_factory):
     d = tmp_path_factory.mktemp("rocrand")
     src, exe = d / "philox_ref.cpp", d / "philox_ref"
     src.write_text(_ROCRAND_PROG)
-    subprocess.run([_HIPCC, "-x", "c++", "-O1", "-I/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
-                    str(src), "-o", str(exe)], check=True, capture_output=True, timeout=300)
+    res = subprocess.run([_HIPCC, "-x", "c++", "-O1", "-I/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
+                          str(src), "-o", str(exe)], capture_output=True, text=True, timeout=300)
+    if res.returncode != 0:
+        pytest.skip("could not build the rocRAND reference program: " + res.stderr[-300:])
 
     def run(ctr, key):
         rows = np.concatenate([ctr, key], axis=1).astype(np.uint64)
