@@ -76,6 +76,49 @@ def make_inputs(shape, dtype, seed: int, mult: float = 1.0):
     return tuple(out)
 
 
+def make_trending_inputs(shape, dtype, seed: int, pattern: str, rise: float):
+    """(Q, K, V, dO) whose scores change steeply along the keys.
+
+    A seeded direction u (entries +-1) is shared by every query and key:
+    Q[i] = a_i u + n/4 and K[j] = r_j u + n/4 with n ~ N(0, 1), so that the
+    score of (i, j) is about a_i r_j d / sqrt(d) plus noise.  ``rise`` is the
+    total change of r_j u.u / sqrt(d) over the sequence.
+
+    * ``"ramp"``: r_j rises linearly over the keys (centred on 0), a_i = 1;
+      every row's largest scores sit at its last visible keys.
+    * ``"spike"``: r_j = 0 except two late keys (N/2 + 3 and N - 5) at
+      r = rise / 2 and rise; a_i = 1.
+    * ``"mixed"``: the ramp, with a_i = (i mod 3) - 1, so rows alternate
+      between rising, flat and falling scores.
+
+    V and dO are N(0, 1).  Values are rounded to ``dtype`` like
+    ``make_inputs``.
+    """
+    B, H, N, d = shape
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    u = torch.randint(0, 2, (d,), generator=g).to(torch.float32) * 2 - 1
+    nq = torch.randn(tuple(shape), generator=g) / 4
+    nk = torch.randn(tuple(shape), generator=g) / 4
+    v = torch.randn(tuple(shape), generator=g)
+    do = torch.randn(tuple(shape), generator=g)
+    step = rise / d ** 0.5
+    j = torch.arange(N, dtype=torch.float32)
+    if pattern == "spike":
+        r = torch.zeros(N)
+        for pos, frac in ((N // 2 + 3, 0.5), (N - 5, 1.0)):
+            if 0 <= pos < N:
+                r[pos] = step * frac
+        a = torch.ones(N)
+    elif pattern in ("ramp", "mixed"):
+        r = step * (j / max(N - 1, 1) - 0.5)
+        a = torch.ones(N) if pattern == "ramp" else (torch.arange(N) % 3 - 1).to(torch.float32)
+    else:
+        raise ValueError(f"unknown pattern {pattern!r}")
+    q = a[:, None] * u[None, :] + nq
+    k = r[:, None] * u[None, :] + nk
+    return tuple(t.to(dtype) for t in (q, k, v, do))
+
+
 def workload_inputs(w: Workload):
     return make_inputs(w.shape, w.dtype, w.seed, w.mult)
 

@@ -278,6 +278,24 @@ def test_tiled_forward_equals_standard(causal, blk):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pattern", ["ramp", "spike", "mixed"])
+def test_tiled_forward_with_moving_maximum_equals_standard(pattern, causal):
+    # scores rising by 150 along the keys: the running maximum moves in most
+    # blocks, so the rescaling by e^(m_old - m_new) carries the result
+    from exact_io_aware_09_amd.workloads import make_trending_inputs
+    q, k, v, _ = (t[0, 0].to(F64) for t in make_trending_inputs((1, 1, 200, 32), torch.float32, 9, pattern, 150.0))
+    scale = 1 / math.sqrt(32)
+    o_ref, lse_ref = A.attention_forward(q, k, v, scale, causal)
+    o1, m1, l1 = T.forward_outer_kv(q, k, v, scale, causal, 32, 32)
+    # relative to the largest log-sum-exp (about 75 here)
+    assert float((o1 - o_ref).abs().max()) < 1e-13
+    assert float((m1 + torch.log(l1) - lse_ref).abs().max()) < 1e-12
+    o2, lse2 = T.forward_outer_q(q, k, v, scale, causal, 32, 32)
+    assert float((o2 - o_ref).abs().max()) < 1e-13
+    assert float((lse2 - lse_ref).abs().max()) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_tiled_backward_equals_standard(causal):
     n, d = 200, 16  # ragged: 200 is not a multiple of 64
     q, k, v, do = (rnd((n, d), s) for s in range(140, 144))
