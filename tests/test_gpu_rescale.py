@@ -18,8 +18,10 @@ happens, so these cases build scores from a shared direction
   a wavefront some rows move their base and others keep it.
 
 O and LSE are checked against the fp64 oracle at the tolerances of the dense
-tests (bf16: 2e-2 and 1e-3 max-abs; fp32: 1e-5).  The key-split forward,
-whose ranges each start a fresh base, is checked on the same inputs.
+tests (bf16: 2e-2 and 1e-3 max-abs; fp32: 1e-5).  The key-split forward
+(whose ranges each start a fresh base), the dropout forward and the
+block-sparse forward take the same base decisions and are checked on the same
+inputs.
 
 Gradients need a different yardstick here.  Every key row carries a large
 shared component along u while sum_j dS_ij = 0, so dQ_i = scale sum_j dS_ij
@@ -141,6 +143,48 @@ def test_split_forward_moving_maximum(pattern, causal):
     o, lse = fa.forward_split(qd, kd, vd, 0.125, causal, splits=4)
     torch.cuda.synchronize()
     ro, rl = A.per_head(A.attention_forward, (q, k, v), 0.125, causal)
+    what = f"{pattern} causal={causal}"
+    assert max_abs(o.cpu(), ro) <= 2e-2, f"{what}: O {max_abs(o.cpu(), ro)}"
+    assert max_abs(lse.cpu(), rl) <= 1e-3, f"{what}: LSE {max_abs(lse.cpu(), rl)}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pattern", PATTERNS)
+def test_dropout_forward_moving_maximum(pattern, causal):
+    # the dropout forward takes the same base decisions before zeroing the
+    # dropped weights; O (scaled by 256/t) and LSE against the oracle
+    from oracle import dropout as DR
+    shape, p, seed = (1, 2, 300, 64), 0.2, 0x5EED
+    q, k, v, do = make_trending_inputs(shape, torch.bfloat16, 90, pattern, 150.0)
+    qd, kd, vd = (x.to(dev()) for x in (q, k, v))
+    o, lse = fa.forward_dropout(qd, kd, vd, 0.125, causal, p, seed)
+    torch.cuda.synchronize()
+    t = DR.keep_threshold(p)
+    keep = DR.keep_masks(seed, 1, 2, 300, t)
+    ro, rl = DR.attention_forward_backward_dropout(q, k, v, do, 0.125, causal, keep, t)[:2]
+    what = f"{pattern} causal={causal}"
+    assert max_abs(o.cpu(), ro) <= 2e-2 * 256 / t, f"{what}: O {max_abs(o.cpu(), ro)}"
+    assert max_abs(lse.cpu(), rl) <= 1e-3, f"{what}: LSE {max_abs(lse.cpu(), rl)}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pattern", PATTERNS)
+def test_sparse_forward_moving_maximum(pattern, causal):
+    # block-sparse walk (band of 128 x 128 tiles plus tile column 0): each
+    # row block's first visited key block sets the base, later set tiles move it
+    shape = (1, 2, 600, 64)
+    q, k, v, do = make_trending_inputs(shape, torch.bfloat16, 100, pattern, 150.0)
+    nb = 5
+    mask = torch.zeros(nb, nb, dtype=torch.int32)
+    for i in range(nb):
+        mask[i, 0] = 1
+        for j in range(max(0, i - 1), min(nb, i + 2)):
+            mask[i, j] = 1
+    qd, kd, vd = (x.to(dev()) for x in (q, k, v))
+    o, lse = fa.forward_sparse(qd, kd, vd, mask.to(dev()).contiguous(), 0.125, causal)
+    torch.cuda.synchronize()
+    vis = A.visible_from_blocks(mask, 600, 128)
+    ro, rl = A.per_head(A.attention_forward_backward_masked, (q, k, v, do), 0.125, causal, vis)[:2]
     what = f"{pattern} causal={causal}"
     assert max_abs(o.cpu(), ro) <= 2e-2, f"{what}: O {max_abs(o.cpu(), ro)}"
     assert max_abs(lse.cpu(), rl) <= 1e-3, f"{what}: LSE {max_abs(lse.cpu(), rl)}"
