@@ -29,3 +29,18 @@ def test_autograd_equals_direct_calls(dtype, causal, p):
     assert torch.equal(o.detach(), o2)
     for g, r in zip((qg.grad, kg.grad, vg.grad), g2):
         assert torch.equal(g, r)
+
+
+def test_readme_example_runs():
+    # the usage example in README.md, executed as written
+    import pathlib
+    import re
+    text = (pathlib.Path(__file__).resolve().parent.parent / "README.md").read_text()
+    blocks = re.findall(r"```python\n(.*?)```", text, flags=re.S)
+    assert blocks, "README has no python example"
+    ns = {}
+    exec(compile(blocks[0], "README.md", "exec"), ns)
+    torch.cuda.synchronize()
+    for name in ("q", "k", "v"):
+        assert ns[name].shape == (2, 16, 1024, 64)
+    assert torch.isfinite(ns["o"].float()).all() and torch.isfinite(ns["dq"].float()).all()
