@@ -948,6 +948,7 @@ hipError_t run_bwd_c(const void* Q, const void* K, const void* V, const void* O,
 
 }  // namespace
 
+#ifndef FA_D256_UNIT
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                 float* Dws, const Problem& p, unsigned stages,
@@ -958,10 +959,19 @@ hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, con
     case 128:
       return run_bwd_c<128, FA_BWD_CFG_D128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream, dr);
     case 256:
-      return run_bwd_c<256, FA_BWD_CFG_D256>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream, dr);
+      return launch_backward_bf16_d256(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream, sp, dr);
     default:
       return hipErrorInvalidValue;
   }
 }
+#else
+// Head dim 256 (this source compiled a second time as fa_bwd_d256.hip)
+hipError_t launch_backward_bf16_d256(const void* Q, const void* K, const void* V, const void* O,
+                                     const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                                     float* Dws, const Problem& p, unsigned stages,
+                                     hipStream_t stream, SparseArgs sp, const DropArgs* dr) {
+  return run_bwd_c<256, FA_BWD_CFG_D256>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream, dr);
+}
+#endif
 
 }  // namespace fa

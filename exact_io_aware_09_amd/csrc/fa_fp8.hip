@@ -468,6 +468,7 @@ hipError_t run_fwd_fp8_c(const void* Q8, const void* Qs, const void* K8, const v
 
 }  // namespace
 
+#ifndef FA_D256_UNIT
 hipError_t launch_quantize_fp8(const void* X, void* X8, void* Xs, const Problem& p, bool keys,
                                hipStream_t stream) {
   const long long BH = (long long)p.B * p.H;
@@ -521,9 +522,17 @@ hipError_t launch_forward_fp8(const void* Q8, const void* Qs, const void* K8, co
   switch (p.d) {
     case 64: return run_fwd_fp8_c<64, FA_FP8_CFG_D64>(Q8, Qs, K8, Ks, V8, Vs, O, LSE, p, stream);
     case 128: return run_fwd_fp8_c<128, FA_FP8_CFG_D128>(Q8, Qs, K8, Ks, V8, Vs, O, LSE, p, stream);
-    case 256: return run_fwd_fp8_c<256, FA_FP8_CFG_D256>(Q8, Qs, K8, Ks, V8, Vs, O, LSE, p, stream);
+    case 256: return launch_forward_fp8_d256(Q8, Qs, K8, Ks, V8, Vs, O, LSE, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
+#else
+// Head dim 256 (this source compiled a second time as fa_fp8_d256.hip)
+hipError_t launch_forward_fp8_d256(const void* Q8, const void* Qs, const void* K8, const void* Ks,
+                                   const void* V8, const void* Vs, void* O, float* LSE,
+                                   const Problem& p, hipStream_t stream) {
+  return run_fwd_fp8_c<256, FA_FP8_CFG_D256>(Q8, Qs, K8, Ks, V8, Vs, O, LSE, p, stream);
+}
+#endif
 
 }  // namespace fa

@@ -652,12 +652,13 @@ hipError_t run_merge(const float* Opart, const float* Lpart, int splits, void* O
 
 }  // namespace
 
+#ifndef FA_D256_UNIT
 hipError_t launch_forward_split_bf16(const void* Q, const void* K, const void* V, const Problem& p,
                                      int splits, float* Opart, float* Lpart, hipStream_t stream) {
   switch (p.d) {
     case 64: return run_fwd_split_c<64, FA_FWD_CFG_D64>(Q, K, V, p, splits, Opart, Lpart, stream);
     case 128: return run_fwd_split_c<128, FA_FWD_CFG_D128>(Q, K, V, p, splits, Opart, Lpart, stream);
-    case 256: return run_fwd_split_c<256, FA_FWD_CFG_D256>(Q, K, V, p, splits, Opart, Lpart, stream);
+    case 256: return launch_forward_split_bf16_d256(Q, K, V, p, splits, Opart, Lpart, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -679,7 +680,7 @@ hipError_t launch_forward_dropout_bf16(const void* Q, const void* K, const void*
   switch (p.d) {
     case 64: return run_fwd_drop_c<64, FA_FWD_CFG_D64>(Q, K, V, O, LSE, p, dr, stream);
     case 128: return run_fwd_drop_c<128, FA_FWD_CFG_D128>(Q, K, V, O, LSE, p, dr, stream);
-    case 256: return run_fwd_drop_c<256, FA_FWD_CFG_D256>(Q, K, V, O, LSE, p, dr, stream);
+    case 256: return launch_forward_dropout_bf16_d256(Q, K, V, O, LSE, p, dr, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -689,9 +690,29 @@ hipError_t launch_forward_bf16(const void* Q, const void* K, const void* V, void
   switch (p.d) {
     case 64: return run_fwd_c<64, FA_FWD_CFG_D64>(Q, K, V, O, LSE, p, stream, sp);
     case 128: return run_fwd_c<128, FA_FWD_CFG_D128>(Q, K, V, O, LSE, p, stream, sp);
-    case 256: return run_fwd_c<256, FA_FWD_CFG_D256>(Q, K, V, O, LSE, p, stream, sp);
+    case 256: return launch_forward_bf16_d256(Q, K, V, O, LSE, p, stream, sp);
     default: return hipErrorInvalidValue;
   }
 }
+#else
+// Head dim 256 (this source compiled a second time as fa_fwd_d256.hip)
+hipError_t launch_forward_split_bf16_d256(const void* Q, const void* K, const void* V,
+                                          const Problem& p, int splits, float* Opart, float* Lpart,
+                                          hipStream_t stream) {
+  return run_fwd_split_c<256, FA_FWD_CFG_D256>(Q, K, V, p, splits, Opart, Lpart, stream);
+}
+
+hipError_t launch_forward_dropout_bf16_d256(const void* Q, const void* K, const void* V, void* O,
+                                            float* LSE, const Problem& p, const DropArgs& dr,
+                                            hipStream_t stream) {
+  return run_fwd_drop_c<256, FA_FWD_CFG_D256>(Q, K, V, O, LSE, p, dr, stream);
+}
+
+hipError_t launch_forward_bf16_d256(const void* Q, const void* K, const void* V, void* O,
+                                    float* LSE, const Problem& p, hipStream_t stream,
+                                    SparseArgs sp) {
+  return run_fwd_c<256, FA_FWD_CFG_D256>(Q, K, V, O, LSE, p, stream, sp);
+}
+#endif
 
 }  // namespace fa

@@ -83,6 +83,26 @@ hipError_t launch_forward_fp8(const void* Q8, const void* Qs, const void* K8, co
                               const void* V8, const void* Vs, void* O, float* LSE,
                               const Problem& p, hipStream_t stream);
 
+// Head dim 256: the same kernels, built in their own units (fa_*_d256.hip)
+// with the matrix instructions' accumulators kept in VGPRs; the launchers
+// above forward d = 256 to these.
+hipError_t launch_forward_bf16_d256(const void* Q, const void* K, const void* V, void* O,
+                                    float* LSE, const Problem& p, hipStream_t stream,
+                                    SparseArgs sp);
+hipError_t launch_forward_dropout_bf16_d256(const void* Q, const void* K, const void* V, void* O,
+                                            float* LSE, const Problem& p, const DropArgs& dr,
+                                            hipStream_t stream);
+hipError_t launch_forward_split_bf16_d256(const void* Q, const void* K, const void* V,
+                                          const Problem& p, int splits, float* Opart, float* Lpart,
+                                          hipStream_t stream);
+hipError_t launch_backward_bf16_d256(const void* Q, const void* K, const void* V, const void* O,
+                                     const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                                     float* Dws, const Problem& p, unsigned stages,
+                                     hipStream_t stream, SparseArgs sp, const DropArgs* dr);
+hipError_t launch_forward_fp8_d256(const void* Q8, const void* Qs, const void* K8, const void* Ks,
+                                   const void* V8, const void* Vs, void* O, float* LSE,
+                                   const Problem& p, hipStream_t stream);
+
 // float32 throughout (vector ALU).
 hipError_t launch_forward_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
                               const Problem& p, hipStream_t stream);
