@@ -215,3 +215,18 @@ def test_forward_fp8_validation(args, code):
               causal=0, stream=None)
     kw.update(args)
     assert fa.fa_forward_fp8(**kw) == code
+
+
+def test_every_kernel_source_is_a_build_unit():
+    # a .hip file left out of the unit list would silently drop its kernels
+    from exact_io_aware_09_amd import build as B
+    on_disk = {p.name for p in B.CSRC.glob("*.hip")}
+    assert on_disk == set(B.SOURCES)
+    # the head-dim-256 units compile their base source with the VGPR form
+    for name, extra in B.UNITS:
+        if name.endswith("_d256.hip"):
+            assert extra == B.VGPR_FORM
+            text = (B.CSRC / name).read_text()
+            assert "#define FA_D256_UNIT" in text and f'#include "{name.replace("_d256", "")}"' in text
+        else:
+            assert extra == []
