@@ -24,7 +24,8 @@ LIB_PATH = PKG_DIR / LIB_NAME
 BUILD_DIR = REPO_DIR / "_build"
 ARCH = "gfx950"
 # Matrix instructions with their accumulators in VGPRs: for the head-dim-256
-# units, whose kernels run one wavefront per SIMD (see fa_fwd_d256.hip).
+# units and the non-causal head-dim-128 backward, whose kernels run one
+# wavefront per SIMD (see fa_fwd_d256.hip, fa_bwd_d128nc.hip).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 # (unit, extra flags)
 UNITS = [
@@ -33,6 +34,7 @@ UNITS = [
     ("fa_fwd_d256.hip", VGPR_FORM),
     ("fa_bwd.hip", []),
     ("fa_bwd_d256.hip", VGPR_FORM),
+    ("fa_bwd_d128nc.hip", VGPR_FORM),
     ("fa_fp8.hip", []),
     ("fa_fp8_d256.hip", VGPR_FORM),
     ("fa_f32.hip", []),

@@ -948,7 +948,7 @@ hipError_t run_bwd_c(const void* Q, const void* K, const void* V, const void* O,
 
 }  // namespace
 
-#ifndef FA_D256_UNIT
+#if !defined(FA_D256_UNIT) && !defined(FA_D128NC_UNIT)
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                 float* Dws, const Problem& p, unsigned stages,
@@ -957,12 +957,23 @@ hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, con
     case 64:
       return run_bwd_c<64, FA_BWD_CFG_D64>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream, dr);
     case 128:
+      if (!p.causal)
+        return launch_backward_bf16_d128nc(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream, sp, dr);
       return run_bwd_c<128, FA_BWD_CFG_D128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream, dr);
     case 256:
       return launch_backward_bf16_d256(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, stream, sp, dr);
     default:
       return hipErrorInvalidValue;
   }
+}
+#elif defined(FA_D128NC_UNIT)
+// Head dim 128 without the causal mask (this source compiled a second time
+// as fa_bwd_d128nc.hip)
+hipError_t launch_backward_bf16_d128nc(const void* Q, const void* K, const void* V, const void* O,
+                                       const void* dO, const float* LSE, void* dQ, void* dK,
+                                       void* dV, float* Dws, const Problem& p, unsigned stages,
+                                       hipStream_t stream, SparseArgs sp, const DropArgs* dr) {
+  return run_bwd_c<128, FA_BWD_CFG_D128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream, dr);
 }
 #else
 // Head dim 256 (this source compiled a second time as fa_bwd_d256.hip)

@@ -99,6 +99,12 @@ hipError_t launch_backward_bf16_d256(const void* Q, const void* K, const void* V
                                      const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                      float* Dws, const Problem& p, unsigned stages,
                                      hipStream_t stream, SparseArgs sp, const DropArgs* dr);
+// Head dim 128 without the causal mask: the backward built with the same
+// VGPR-form matrix instructions (its dK/dV runs one wavefront per SIMD).
+hipError_t launch_backward_bf16_d128nc(const void* Q, const void* K, const void* V, const void* O,
+                                       const void* dO, const float* LSE, void* dQ, void* dK,
+                                       void* dV, float* Dws, const Problem& p, unsigned stages,
+                                       hipStream_t stream, SparseArgs sp, const DropArgs* dr);
 hipError_t launch_forward_fp8_d256(const void* Q8, const void* Qs, const void* K8, const void* Ks,
                                    const void* V8, const void* Vs, void* O, float* LSE,
                                    const Problem& p, hipStream_t stream);
