@@ -122,15 +122,25 @@ def forward_outer_kv(q, k, v, scale, causal, br, bc, io: IOCount | None = None, 
     return o, m, l
 
 
-def forward_outer_q(q, k, v, scale, causal, br, bc):
-    """Tiled forward, Q outer loop, unnormalised accumulator; (O, LSE)."""
+def forward_outer_q(q, k, v, scale, causal, br, bc, io: IOCount | None = None):
+    """Tiled forward, Q outer loop, unnormalised accumulator; (O, LSE).
+
+    ``io`` counts the elements of the N x d matrices that the loop moves:
+    Q_i read once per Q block, K_j and V_j read once per visited (i, j)
+    pair, O_i written once.  The row statistics (LSE, N elements written
+    once) are left out of the count, as in the lab-bench traffic model of
+    "FlashAttention and GPU memory", section 14.
+    """
     q, k, v = (t.to(_F64) for t in (q, k, v))
     n, d = q.shape
+    io = io if io is not None else IOCount()
     o = torch.empty(n, d, dtype=_F64)
     lse = torch.empty(n, dtype=_F64)
     for i0 in range(0, n, br):
         i1 = min(n, i0 + br)
         rows = i1 - i0
+        qi = q[i0:i1]
+        io.reads += rows * d
         m = torch.full((rows,), float("-inf"), dtype=_F64)
         l = torch.zeros(rows, dtype=_F64)
         acc = torch.zeros(rows, d, dtype=_F64)
@@ -138,16 +148,20 @@ def forward_outer_q(q, k, v, scale, causal, br, bc):
             if not _visible(i0, i1, j0, causal):
                 break
             j1 = min(n, j0 + bc)
-            s = _mask_block(scale * (q[i0:i1] @ k[j0:j1].T), i0, j0, causal)
+            kj, vj = k[j0:j1], v[j0:j1]
+            io.reads += 2 * (j1 - j0) * d
+            io.pairs += 1
+            s = _mask_block(scale * (qi @ kj.T), i0, j0, causal)
             m_new = torch.maximum(m, s.max(dim=1).values)
             # rows still without a visible key keep m = -inf; use base 0 there
             base = torch.where(torch.isinf(m_new), torch.zeros_like(m_new), m_new)
             p = torch.exp(s - base.unsqueeze(1))
             alpha = torch.where(torch.isinf(m), torch.zeros_like(m), torch.exp(m - base))
             l = alpha * l + p.sum(dim=1)
-            acc = alpha.unsqueeze(1) * acc + p @ v[j0:j1]
+            acc = alpha.unsqueeze(1) * acc + p @ vj
             m = m_new
         o[i0:i1] = acc / l.unsqueeze(1)
+        io.writes += rows * d
         lse[i0:i1] = m + torch.log(l)
     return o, lse
 

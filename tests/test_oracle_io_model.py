@@ -100,9 +100,22 @@ def test_credited_flops():
     assert bwd == fwd * 5 // 2
 
 
-def test_second_version_traffic_model():
-    # Q once, K and V once per Q block, O once (no cache credit)
-    n, d, br = 1024, 64, 128
-    assert IO.second_version_uncached(n, d, br) == 2 * n * d + (n // br) * 2 * n * d
-    causal = IO.second_version_uncached(n, d, br, causal=True)
-    assert causal == 2 * n * d + sum(2 * (i + 1) * br * d for i in range(n // br))
+@pytest.mark.parametrize("n,d,br,bc", [(256, 16, 64, 16), (200, 8, 64, 32), (97, 4, 32, 32),
+                                        (130, 8, 128, 64), (64, 4, 64, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_second_version_traffic_model_counts_the_tiled_loop(n, d, br, bc, causal):
+    # The lab-bench model ("FlashAttention and GPU memory", section 14) against
+    # an independent count: the elements the Q-outer tiled forward actually
+    # slices out of Q, K, V and writes to O, block by block.  K/V block widths
+    # divide the query block, so a causal query block ending at row i1 reads
+    # exactly the key rows [0, i1); N is ragged in several cases.
+    g = torch.Generator().manual_seed(n * 131 + d)
+    q, k, v = (torch.randn(n, d, generator=g, dtype=torch.float64) for _ in range(3))
+    io = T.IOCount()
+    T.forward_outer_q(q, k, v, 0.5, causal, br, bc, io=io)
+    assert io.total == IO.second_version_uncached(n, d, br, causal=causal)
+    # every visited (i, j) pair read its K and V blocks exactly once
+    nq = -(-n // br)
+    full = nq * (-(-n // bc))
+    assert io.pairs == (full if not causal else
+                        sum(-(-min(n, (i + 1) * br) // bc) for i in range(nq)))
