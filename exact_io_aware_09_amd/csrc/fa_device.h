@@ -123,6 +123,36 @@ __device__ __forceinline__ void grouped_order(int L, int nblk, int BH, int G, in
   rank = r / gh;
 }
 
+// Persistent launches: the grid holds as many workgroups as the GPU keeps
+// resident at once, a multiple of the XCD count, and every workgroup loops
+// over tiles, prefetching the next tile's inputs while it computes the
+// current one (so the compulsory device-memory traffic of tile starts and
+// ends overlaps the matrix work instead of running between tiles).
+// Workgroup b runs on XCD b mod 8 and walks that XCD's contiguous range of
+// logical tiles (the same partition as xcd_remap) in rounds of one tile per
+// workgroup of the XCD, in snake order: position i in even rounds,
+// gx - 1 - i in odd ones.  Logical tiles come longest-first within a head
+// group (grouped_order), so over two rounds each workgroup takes one long
+// and one short causal tile.  Every tile of the range is visited exactly
+// once (each round is a permutation of the workgroup positions), the tile
+// index grows with the round, and -1 marks the end.
+struct PersistOrder {
+  int lo, cnt, gx, i;
+  __device__ __forceinline__ PersistOrder(int b, int grid, int total) {
+    const int x = b % kNumXcd;
+    i = b / kNumXcd;
+    gx = grid / kNumXcd;
+    const int q = total / kNumXcd, r = total % kNumXcd;
+    lo = x * q + (x < r ? x : r);
+    cnt = q + (x < r ? 1 : 0);
+  }
+  __device__ __forceinline__ int tile(int n) const {
+    const int pos = (n & 1) ? gx - 1 - i : i;
+    const long long j = (long long)n * gx + pos;
+    return j < cnt ? lo + (int)j : -1;
+  }
+};
+
 // Offsets of the blocks (BSZ rows or keys each, BSZ dividing 128) that a
 // workgroup visits in its main loop.  Dense: every block from `start` below
 // `end`.  Block-sparse: only the blocks inside the set 128 x 128 tiles of
@@ -321,25 +351,61 @@ __device__ __forceinline__ void lds_copy4(copy_rsrc r, uint32_t voff, uint32_t l
       : "memory");
 }
 
+// As lds_copy16, with the byte offset split into a per-lane part (VGPR) and
+// a part that is the same in every lane (SGPR; callers pass wave-uniform
+// values).
+__device__ __forceinline__ void lds_copy16_s(copy_rsrc r, uint32_t voff, uint32_t soff, uint32_t lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "memory");
+}
+
 // Copy of one [ROWS x D] bf16 block (rows r0.. of the descriptor's tensor)
 // into a swizzled LDS tile, without VGPRs.  Each wavefront instruction
 // writes 64 x 16 bytes to consecutive LDS addresses, so lane L fetches the
 // global chunk that the swizzle places at that position.  Rows past the end
 // of the descriptor read as zeros.  CHUNKS / NT copies per lane.
+// Head dim 64: a 1 KB block holds 8 rows and the swizzle repeats every 16
+// rows, so with an even number of wavefronts the blocks a wavefront writes
+// all start at the same phase of the swizzle (block w + i * NWAVE starts at
+// row 8 (w mod 2) mod 16).  Lane L then fetches the same chunk of its row
+// in every block: one per-lane byte offset for all the copies (and all
+// tiles of the kernel), the rest of the offset uniform (SGPR).
 template <int D, int ROWS, int NT>
 __device__ __forceinline__ void dma_tile(copy_rsrc r, int r0, bf16_t* tile, int tid) {
   constexpr int CPR = D / 8;               // chunks per row
   constexpr int CHUNKS = ROWS * CPR;
   constexpr int NWAVE = NT / kWave;
   static_assert(CHUNKS % NT == 0, "block must split evenly over the threads");
-  const int w = tid >> 6, lane = tid & 63;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if constexpr (D == 64 && NWAVE % 2 == 0) {
+    constexpr int RPB = kWave / CPR;       // rows per 1 KB block: 8
+    const int lrow = lane / CPR;
+    const int srow = ((w * RPB) & 15) + lrow;  // row within the swizzle's 16-row period
+    const uint32_t voff = (uint32_t)(lrow * D + ((lane % CPR) ^ swz<D>(srow)) * 8) * 2u;
 #pragma unroll
-  for (int i = 0; i < CHUNKS / NT; ++i) {
-    const int blk = w + i * NWAVE;           // 1 KB block of the tile written by this instruction
-    const int pos = blk * 64 + lane;         // chunk position in LDS
-    const int row = pos / CPR, c = (pos % CPR) ^ swz<D>(row);
-    const uint32_t goff = ((uint32_t)(r0 + row) * D + c * 8) * 2u;
-    lds_copy16(r, goff, lds_address(tile + blk * 512));
+    for (int i = 0; i < CHUNKS / NT; ++i) {
+      const int blk = w + i * NWAVE;
+      const uint32_t soff = (uint32_t)(r0 + blk * RPB) * (D * 2u);
+      lds_copy16_s(r, voff, soff, lds_address(tile + blk * 512));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CHUNKS / NT; ++i) {
+      const int blk = w + i * NWAVE;           // 1 KB block of the tile written by this instruction
+      const int pos = blk * 64 + lane;         // chunk position in LDS
+      const int row = pos / CPR, c = (pos % CPR) ^ swz<D>(row);
+      const uint32_t goff = ((uint32_t)(r0 + row) * D + c * 8) * 2u;
+      lds_copy16(r, goff, lds_address(tile + blk * 512));
+    }
   }
 }
 

@@ -50,6 +50,12 @@ namespace {
 
 constexpr float kMaxWeight = 65536.0f;  // bound on one lane's share of a block's row sum
 
+// Dense forwards whose Q blocks fit the LDS staging tile run persistent.
+#ifndef FA_FWD_PERSISTENT
+#define FA_FWD_PERSISTENT 1
+#endif
+constexpr bool kFwdPersistent = FA_FWD_PERSISTENT != 0;
+
 template <int D, int NW, int RB, int BC, int ST>
 struct FwdCfg {
   static constexpr int NT = NW * kWave;        // threads per workgroup
@@ -67,11 +73,229 @@ struct FwdCfg {
   static_assert(ST >= 2 && ST <= 3, "two or three K/V stages");
 };
 
-// Per block t: S^T = K Q^T, mask, online softmax, O^T += V^T P^T, with the
-// K/V blocks of the next ST-1 steps in flight (direct buffer->LDS loads).
-// A wavefront owns RB blocks of 32 query rows: every K and V fragment read
-// from LDS feeds RB matrix instructions, which divides LDS reads and
-// HBM->LDS copies per FLOP by RB.
+// Per-wavefront state and per-block work of the forward: RB blocks of 32
+// query rows (first row q0w), their Q fragments (B operands of S^T = K Q^T,
+// lane = query row), the running maximum m and row sum l of each row (the
+// lane's half of the row), and the unnormalised output O^T.  Every K and V
+// fragment read from LDS feeds the RB row blocks, which divides LDS reads
+// and HBM->LDS copies per FLOP by RB.
+template <int D, int NW, int RB, int BC, int ST, bool CAUSAL, bool SPLIT, bool DROP>
+struct FwdWave {
+  using C = FwdCfg<D, NW, RB, BC, ST>;
+  bf16x8 qf[RB][C::KSTEPS];
+  f32x16 oacc[RB][C::DB];
+  float m[RB], l[RB];
+  int q0w, N, lane, h, c32;
+  float c;
+
+  // Base of the exponent.  Every row sees key 0 of its first block, so m is
+  // finite -- except for a key range that starts after a causal row, which
+  // sees nothing of the range: its weights are then exp2(-inf) = 0.
+  __device__ __forceinline__ static float base(float mrow) {
+    return (SPLIT && CAUSAL && mrow == -INFINITY) ? 0.f : mrow;
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
+      m[rb] = -INFINITY;
+      l[rb] = 0.f;
+    }
+  }
+
+  // Q fragments of this wavefront's rows from a row-major staging tile
+  // (row 0 of the tile = query row q0w - row0).
+  __device__ __forceinline__ void load_q(const bf16_t* qs, int row0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) qf[rb][s] = frag_rows<D>(qs, row0 + 32 * rb, 16 * s, c32, h);
+  }
+
+  // S^T = K Q^T for the block at key j0 (lane: query; registers: keys), each
+  // K fragment feeding the RB row blocks; causal-future keys and keys past
+  // the end become -inf, on the blocks that need it only.
+  __device__ __forceinline__ void scores(const bf16_t* Ks, int j0, f32x16 (&sacc)[RB][C::KB]) const {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      bf16x8 kfr[C::KSTEPS];
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) kfr[s] = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
+      const f32x16 z = {};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[0], qf[rb][0], z);
+#pragma unroll
+      for (int s = 1; s < C::KSTEPS; ++s)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[s], qf[rb][s], sacc[rb][kb]);
+    }
+    const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
+    if (need_mask) {
+      keep_branch();
+      const int nk = N - j0 - 4 * h;  // key >= N  <=>  key offset >= nk
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        // key - query = kq + key offset; future keys and keys past the end
+        // both have key offset > lim
+        const int kq = j0 + 4 * h - (q0w + 32 * rb + c32);
+        const int lim = CAUSAL ? min(-kq, nk - 1) : nk - 1;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
+            if (koff > lim) sacc[rb][kb][r] = -INFINITY;
+          }
+      }
+    }
+  }
+
+  // Row maximum of a block, scaled to log2 units (both halves of the row).
+  __device__ __forceinline__ float block_max(const f32x16 (&sacc)[C::KB]) const {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    return max_halves(mx) * c;
+  }
+
+  // P^T = exp2(c S^T - m) in place; returns this lane's share of the row sum.
+  __device__ __forceinline__ float exponentiate(f32x16 (&sacc)[C::KB], float mrow) const {
+    float part[C::KB * 8];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c, -mrow));
+        sacc[kb][r + 1] = fast_exp2(fmaf(sacc[kb][r + 1], c, -mrow));
+        part[kb * 8 + r / 2] = sacc[kb][r] + sacc[kb][r + 1];
+      }
+#pragma unroll
+    for (int n = C::KB * 8; n > 1; n /= 2)
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
+    return part[0];
+  }
+
+  // The block at key j0, the t-th of this tile's walk (t = 0: first block):
+  // scores, online softmax, O^T += V^T P^T.
+  __device__ __forceinline__ void block(int t, int j0, const bf16_t* Ks, const bf16_t* Vs, int bh,
+                                        const DropArgs& dr) {
+    const bool active = !CAUSAL || j0 <= q0w + C::RW - 1;
+    if (!active) return;
+    f32x16 sacc[RB][C::KB];
+    scores(Ks, j0, sacc);
+    // Running maximum m (log2 units): taken from a row's first block
+    // (which always holds key 0, so it is finite) and afterwards kept
+    // while every exponentiated score of the row stays below kMaxWeight;
+    // numerator and denominator share the base, so O and the
+    // log-sum-exp do not depend on when m is raised.
+    if (t == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) m[rb] = block_max(sacc[rb]);
+    }
+    float rs[RB];
+    bool over = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      rs[rb] = exponentiate(sacc[rb], base(m[rb]));
+      over |= !(rs[rb] <= kMaxWeight);
+    }
+    if (wave_any(over)) {
+      // Some row overflowed the bound: rows whose own share (either half)
+      // did so take the block's maximum, rescale O and l, and are
+      // exponentiated again; the other rows recompute the same values.
+      keep_branch();
+      f32x16 s2[RB][C::KB];
+      scores(Ks, j0, s2);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const bool own = !(rs[rb] <= kMaxWeight);
+        const bool row = max_halves(own ? 1.f : 0.f) > 0.f;
+        const float mx = block_max(s2[rb]);
+        if (row) {
+          const float alpha = fast_exp2(m[rb] - mx);
+          m[rb] = mx;
+          l[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+        }
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) sacc[rb][kb] = s2[rb][kb];
+        rs[rb] = exponentiate(sacc[rb], base(m[rb]));
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l[rb] += rs[rb];
+    if constexpr (DROP) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          uint32_t dw[4];
+          draws_query_cols(q0w + 32 * rb, j0 + 32 * kb, bh, lane, dr.k0, dr.k1, dw);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!kept(dw, r, dr.thresh)) sacc[rb][kb][r] = 0.f;
+        }
+    }
+
+    // P^T as B operand (k-step u: registers 8*(u&1).. of key block u>>1,
+    // i.e. keys 16u + 8*(e>>2) + 4h + (e&3)), rounded to bf16, then
+    // O^T += V^T P^T with each V fragment feeding the RB row blocks.
+#pragma unroll
+    for (int u = 0; u < C::PU; ++u) {
+      bf16x8 pf[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const f32x16& pv = sacc[rb][u >> 1];
+        const int r0 = 8 * (u & 1);
+        pf[rb] = bf16x8_from(pack_bf16x2(pv[r0], pv[r0 + 1]), pack_bf16x2(pv[r0 + 2], pv[r0 + 3]),
+                             pack_bf16x2(pv[r0 + 4], pv[r0 + 5]), pack_bf16x2(pv[r0 + 6], pv[r0 + 7]));
+      }
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const bf16x8 vfr = frag_tr<D>(Vs, 16 * u, db * 32, lane);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32x32x16(vfr, pf[rb], oacc[rb][db]);
+      }
+    }
+  }
+
+  // O = acc / l (bf16) straight from the fragments (dims db*32 + 8g + 4h +
+  // 0..3 of this lane's row) and LSE = m ln2 + ln l (fp32, natural log).
+  __device__ __forceinline__ void store(bf16_t* Oh, float* LSEh, float oscale) const {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int query = q0w + 32 * rb + c32;
+      const float lt = sum_halves(l[rb]);  // >= 1: the row maximum has weight >= 1
+      const float inv = __builtin_amdgcn_rcpf(lt) * oscale;
+      if (query < N) {
+        bf16_t* Or = Oh + (size_t)query * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t lo = pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv);
+            const uint32_t hi = pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
+            *reinterpret_cast<uint2*>(Or + db * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
+          }
+        if (h == 0) LSEh[query] = (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2;
+      }
+    }
+  }
+};
+
+// One workgroup per query block (tile), loop over the K/V blocks of the
+// tile with the blocks of the next ST-1 steps in flight (direct
+// buffer->LDS loads).  A wavefront owns RB blocks of 32 query rows.
 //
 // SPLIT: the keys are cut into ranges of sa.span keys (a multiple of 64);
 // workgroup (tile, range) runs the loop over its range only and writes the
@@ -114,7 +338,8 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     else if constexpr (decltype(S)::value == 1) return v1s;
     else return v2s;
   };
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, uniform
   const int h = lane >> 5, c32 = lane & 31;
   int bh, rank, split = 0;
   if constexpr (SPLIT) {
@@ -132,7 +357,14 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   const auto rv = make_copy_rsrc(V + hoff, head_bytes);
 
   const int q0 = qb * C::BR;
-  const int q0w = q0 + w * C::RW;  // first query row of this wavefront
+  FwdWave<D, NW, RB, BC, ST, CAUSAL, SPLIT, DROP> wv;
+  wv.q0w = q0 + w * C::RW;  // first query row of this wavefront
+  wv.N = N;
+  wv.lane = lane;
+  wv.h = h;
+  wv.c32 = c32;
+  wv.c = c;
+  const int q0w = wv.q0w;
   // this lane's query row in row block rb is q0w + 32 * rb + c32
 
   // keys [kbase, kend) of this workgroup: blocks kbase + t*BC, t < ntiles
@@ -188,7 +420,6 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   // The first K/V copies go out before Q is read, so that the latencies
   // overlap.
   fetch_at(jfirst, std::integral_constant<int, 0>{});
-  bf16x8 qf[RB][C::KSTEPS];  // B operands of S^T = K Q^T (lane = query row)
   if constexpr (C::QL) {
     // Q block copied row-major (coalesced) into LDS, rows past N as zeros
     dma_tile<D, C::BR, C::NT>(make_copy_rsrc(Q + hoff, head_bytes), q0, qs, tid);
@@ -198,7 +429,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s)
-        qf[rb][s] = as_bf16x8(
+        wv.qf[rb][s] = as_bf16x8(
             buf_load16(rq, ((uint32_t)(q0w + 32 * rb + c32) * D + 16 * s + 8 * h) * 2u));
     // Q resident here: the compiler does not count the copies, so its own
     // waits for Q must not fall inside the loop (where they would also
@@ -206,101 +437,16 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) pin_ready(qf[rb][s]);
+      for (int s = 0; s < C::KSTEPS; ++s) pin_ready(wv.qf[rb][s]);
   }
   if constexpr (ST > 2) {
     if (1 < ntiles) fetch(1, std::integral_constant<int, 1>{});
   }
   wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - 1));
   ring_barrier();
-  if constexpr (C::QL) {
-    // each wavefront reads (and later overwrites with O) only its own rows
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s)
-        qf[rb][s] = frag_rows<D>(qs, w * C::RW + 32 * rb, 16 * s, c32, h);
-  }
-
-  f32x16 oacc[RB][C::DB];
-  float m[RB], l[RB];
-  // Base of the exponent.  Every row sees key 0 of its first block, so m is
-  // finite -- except for a key range that starts after a causal row, which
-  // sees nothing of the range: its weights are then exp2(-inf) = 0.
-  auto base = [](float mrow) { return (SPLIT && CAUSAL && mrow == -INFINITY) ? 0.f : mrow; };
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
-    m[rb] = -INFINITY;
-    l[rb] = 0.f;
-  }
-
-  // S^T = K Q^T for the block at key j0 (lane: query; registers: keys), each
-  // K fragment feeding the RB row blocks; causal-future keys and keys past
-  // the end become -inf, on the blocks that need it only.
-  auto scores = [&](const bf16_t* Ks, int j0, f32x16 (&sacc)[RB][C::KB]) {
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      bf16x8 kfr[C::KSTEPS];
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) kfr[s] = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
-      const f32x16 z = {};
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[0], qf[rb][0], z);
-#pragma unroll
-      for (int s = 1; s < C::KSTEPS; ++s)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[s], qf[rb][s], sacc[rb][kb]);
-    }
-    const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
-    if (need_mask) {
-      keep_branch();
-      const int nk = N - j0 - 4 * h;  // key >= N  <=>  key offset >= nk
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        // key - query = kq + key offset; future keys and keys past the end
-        // both have key offset > lim
-        const int kq = j0 + 4 * h - (q0w + 32 * rb + c32);
-        const int lim = CAUSAL ? min(-kq, nk - 1) : nk - 1;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
-            if (koff > lim) sacc[rb][kb][r] = -INFINITY;
-          }
-      }
-    }
-  };
-  // Row maximum of a block, scaled to log2 units (both halves of the row).
-  auto block_max = [&](const f32x16 (&sacc)[C::KB]) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    return max_halves(mx) * c;
-  };
-  // P^T = exp2(c S^T - m) in place; returns this lane's share of the row sum.
-  auto exponentiate = [&](f32x16 (&sacc)[C::KB], float mrow) {
-    float part[C::KB * 8];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c, -mrow));
-        sacc[kb][r + 1] = fast_exp2(fmaf(sacc[kb][r + 1], c, -mrow));
-        part[kb * 8 + r / 2] = sacc[kb][r] + sacc[kb][r + 1];
-      }
-#pragma unroll
-    for (int n = C::KB * 8; n > 1; n /= 2)
-#pragma unroll
-      for (int i = 0; i < n / 2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
-    return part[0];
-  };
+  // each wavefront reads (and later overwrites with O) only its own rows
+  if constexpr (C::QL) wv.load_q(qs, w * C::RW);
+  wv.reset();
 
   // Step t on the block at key j0; jn is the next block's key (SPARSE: it
   // is copied in during this step; -1 when this is the last).
@@ -312,90 +458,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     } else {
       if (t + ST - 1 < ntiles) fetch(t + ST - 1, std::integral_constant<int, SN>{});
     }
-    const bool active = !CAUSAL || j0 <= q0w + C::RW - 1;
-    if (active) {
-      const bf16_t* Ks = kst(S);
-      const bf16_t* Vs = vst(S);
-      f32x16 sacc[RB][C::KB];
-      scores(Ks, j0, sacc);
-      // Running maximum m (log2 units): taken from a row's first block
-      // (which always holds key 0, so it is finite) and afterwards kept
-      // while every exponentiated score of the row stays below kMaxWeight;
-      // numerator and denominator share the base, so O and the
-      // log-sum-exp do not depend on when m is raised.
-      if (t == 0) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) m[rb] = block_max(sacc[rb]);
-      }
-      float rs[RB];
-      bool over = false;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        rs[rb] = exponentiate(sacc[rb], base(m[rb]));
-        over |= !(rs[rb] <= kMaxWeight);
-      }
-      if (wave_any(over)) {
-        // Some row overflowed the bound: rows whose own share (either half)
-        // did so take the block's maximum, rescale O and l, and are
-        // exponentiated again; the other rows recompute the same values.
-        keep_branch();
-        f32x16 s2[RB][C::KB];
-        scores(Ks, j0, s2);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const bool own = !(rs[rb] <= kMaxWeight);
-          const bool row = max_halves(own ? 1.f : 0.f) > 0.f;
-          const float mx = block_max(s2[rb]);
-          if (row) {
-            const float alpha = fast_exp2(m[rb] - mx);
-            m[rb] = mx;
-            l[rb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
-          }
-#pragma unroll
-          for (int kb = 0; kb < C::KB; ++kb) sacc[rb][kb] = s2[rb][kb];
-          rs[rb] = exponentiate(sacc[rb], base(m[rb]));
-        }
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) l[rb] += rs[rb];
-      if constexpr (DROP) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int kb = 0; kb < C::KB; ++kb) {
-            uint32_t dw[4];
-            draws_query_cols(q0w + 32 * rb, j0 + 32 * kb, bh, lane, dr.k0, dr.k1, dw);
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (!kept(dw, r, dr.thresh)) sacc[rb][kb][r] = 0.f;
-          }
-      }
-
-      // P^T as B operand (k-step u: registers 8*(u&1).. of key block u>>1,
-      // i.e. keys 16u + 8*(e>>2) + 4h + (e&3)), rounded to bf16, then
-      // O^T += V^T P^T with each V fragment feeding the RB row blocks.
-#pragma unroll
-      for (int u = 0; u < C::PU; ++u) {
-        bf16x8 pf[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const f32x16& pv = sacc[rb][u >> 1];
-          const int r0 = 8 * (u & 1);
-          pf[rb] = bf16x8_from(pack_bf16x2(pv[r0], pv[r0 + 1]), pack_bf16x2(pv[r0 + 2], pv[r0 + 3]),
-                               pack_bf16x2(pv[r0 + 4], pv[r0 + 5]), pack_bf16x2(pv[r0 + 6], pv[r0 + 7]));
-        }
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 vfr = frag_tr<D>(Vs, 16 * u, db * 32, lane);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32x32x16(vfr, pf[rb], oacc[rb][db]);
-        }
-      }
-    }
+    wv.block(t, j0, kst(S), vst(S), bh, dr);
     // step t+1 must be resident; later steps may still be in flight
     if (SPARSE ? jn >= 0 : t + 1 < ntiles) {
       wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(SPARSE ? 0 : min(ST - 2, ntiles - t - 2));
@@ -432,7 +495,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int query = q0w + 32 * rb + c32;
-      const float lt = sum_halves(l[rb]);
+      const float lt = sum_halves(wv.l[rb]);
       const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
       if (query < N) {
         const size_t r = split * rows + (size_t)bh * N + query;
@@ -442,56 +505,166 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 #pragma unroll
           for (int g = 0; g < 4; ++g)
             *reinterpret_cast<float4*>(Op + db * 32 + 8 * g + 4 * h) =
-                make_float4(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv,
-                            oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
-        if (h == 0) sa.Lpart[r] = lt > 0.f ? (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+                make_float4(wv.oacc[rb][db][4 * g] * inv, wv.oacc[rb][db][4 * g + 1] * inv,
+                            wv.oacc[rb][db][4 * g + 2] * inv, wv.oacc[rb][db][4 * g + 3] * inv);
+        if (h == 0) sa.Lpart[r] = lt > 0.f ? (wv.m[rb] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
       }
     }
     return;
   }
 
-  // Epilogue: O = acc / l (bf16), LSE = m ln2 + ln l (fp32, natural log).
+  if constexpr (!C::QL) {
+    wv.store(O + hoff, LSE + (size_t)bh * N, DROP ? dr.scale : 1.f);
+    return;
+  }
+  // Epilogue through LDS: O = acc / l (bf16), LSE = m ln2 + ln l (fp32,
+  // natural log).
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int query = q0w + 32 * rb + c32;
-    const float lt = sum_halves(l[rb]);  // >= 1: the row maximum has weight >= 1
+    const float lt = sum_halves(wv.l[rb]);  // >= 1: the row maximum has weight >= 1
     const float inv = DROP ? __builtin_amdgcn_rcpf(lt) * dr.scale : __builtin_amdgcn_rcpf(lt);
-    if constexpr (C::QL) {
-      // O fragment (dims db*32 + 8g + 4h + 0..3 of this lane's row) into
-      // this wavefront's rows of the Q staging tile
+    // O fragment (dims db*32 + 8g + 4h + 0..3 of this lane's row) into
+    // this wavefront's rows of the Q staging tile
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t lo = pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv);
-          const uint32_t hi = pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
-          *reinterpret_cast<uint2*>(qs + tile_off<D>(w * C::RW + 32 * rb + c32, db * 32 + 8 * g + 4 * h)) =
-              make_uint2(lo, hi);
-        }
-    } else if (query < N) {
-      bf16_t* Or = O + hoff + (size_t)query * D;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t lo = pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv);
-          const uint32_t hi = pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
-          *reinterpret_cast<uint2*>(Or + db * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
-        }
-    }
-    if (h == 0 && query < N) LSE[(size_t)bh * N + query] = (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2;
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = pack_bf16x2(wv.oacc[rb][db][4 * g] * inv, wv.oacc[rb][db][4 * g + 1] * inv);
+        const uint32_t hi = pack_bf16x2(wv.oacc[rb][db][4 * g + 2] * inv, wv.oacc[rb][db][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(qs + tile_off<D>(w * C::RW + 32 * rb + c32, db * 32 + 8 * g + 4 * h)) =
+            make_uint2(lo, hi);
+      }
+    if (h == 0 && query < N) LSE[(size_t)bh * N + query] = (wv.m[rb] + __builtin_amdgcn_logf(lt)) * kLn2;
   }
-  if constexpr (C::QL) {
-    // rows back out of LDS as whole 16-byte chunks: 8 lanes per row, so each
-    // store instruction writes 8 complete rows
-    constexpr int CPR = D / 8;
+  // rows back out of LDS as whole 16-byte chunks: 8 lanes per row, so each
+  // store instruction writes 8 complete rows
+  constexpr int CPR = D / 8;
 #pragma unroll
-    for (int i = 0; i < C::RW * CPR / kWave; ++i) {
-      const int chunk = i * kWave + lane;
-      const int r = chunk / CPR, cc = chunk % CPR;
-      const uint4 v = *reinterpret_cast<const uint4*>(qs + tile_off<D>(w * C::RW + r, cc * 8));
-      if (q0w + r < N) *reinterpret_cast<uint4*>(O + hoff + (size_t)(q0w + r) * D + cc * 8) = v;
-    }
+  for (int i = 0; i < C::RW * CPR / kWave; ++i) {
+    const int chunk = i * kWave + lane;
+    const int r = chunk / CPR, cc = chunk % CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(qs + tile_off<D>(w * C::RW + r, cc * 8));
+    if (q0w + r < N) *reinterpret_cast<uint4*>(O + hoff + (size_t)(q0w + r) * D + cc * 8) = v;
+  }
+}
+
+// Persistent forward: gridDim.x workgroups (as many as stay resident) each
+// loop over query-block tiles in PersistOrder.  Two K/V stages; the K/V
+// ring runs on across tile boundaries (the last step of a tile copies the
+// first K/V block of the next tile, in the next tile's head), the next
+// tile's Q block is copied into the Q staging tile two steps before the end
+// (its rows are in registers by then), and O leaves straight from the
+// fragments, so a tile's inputs arrive and its outputs drain while the
+// matrix cores work.  The arithmetic of every tile is that of
+// fwd_bf16_kernel, so the results are bit for bit the same.
+template <int D, int NW, int RB, int BC, int OCC, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(NW * 64, OCC)
+void fwd_bf16_persistent_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
+                                const bf16_t* __restrict__ V, bf16_t* __restrict__ O,
+                                float* __restrict__ LSE, int BH, int N, int nqb, int G, float c,
+                                DropArgs dr) {
+  using C = FwdCfg<D, NW, RB, BC, 2>;
+  static_assert(C::QL, "the persistent forward stages Q blocks in LDS");
+  __shared__ __attribute__((aligned(16))) bf16_t k0s[C::TILE], v0s[C::TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t k1s[C::TILE], v1s[C::TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t qs[C::BR * D];
+  constexpr int QLOADS = C::BR * D / 8 / C::NT;  // Q-block copies per lane
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, uniform
+  const PersistOrder po(blockIdx.x, gridDim.x, BH * nqb);
+  int L = po.tile(0);
+  if (L < 0) return;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  auto decode = [&](int Lt, int& bh_, int& qb_) {
+    int rank;
+    grouped_order(Lt, nqb, BH, G, bh_, rank);
+    qb_ = CAUSAL ? (nqb - 1 - rank) : rank;  // longest causal blocks first
+  };
+  int bh, qb;
+  decode(L, bh, qb);
+  auto rk = make_copy_rsrc(K + (size_t)bh * N * D, head_bytes);
+  auto rv = make_copy_rsrc(V + (size_t)bh * N * D, head_bytes);
+  dma_tile<D, BC, C::NT>(rk, 0, k0s, tid);
+  dma_tile<D, BC, C::NT>(rv, 0, v0s, tid);
+  dma_tile<D, C::BR, C::NT>(make_copy_rsrc(Q + (size_t)bh * N * D, head_bytes), qb * C::BR, qs, tid);
+  wait_vmem_all();
+  ring_barrier();
+
+  FwdWave<D, NW, RB, BC, 2, CAUSAL, false, DROP> wv;
+  wv.N = N;
+  wv.lane = lane;
+  wv.h = lane >> 5;
+  wv.c32 = lane & 31;
+  wv.c = c;
+  auto kst = [&](auto S) -> bf16_t* {
+    if constexpr (decltype(S)::value == 0) return k0s;
+    else return k1s;
+  };
+  auto vst = [&](auto S) -> bf16_t* {
+    if constexpr (decltype(S)::value == 0) return v0s;
+    else return v1s;
+  };
+  int stage = 0;  // stage holding the tile's first K/V block
+  for (int n = 0;; ++n) {
+    const int q0 = qb * C::BR;
+    wv.q0w = q0 + w * C::RW;
+    wv.load_q(qs, w * C::RW);
+    wv.reset();
+    const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
+    const int nt = (kend + BC - 1) / BC;
+    const int Ln = po.tile(n + 1);
+    int bhn = bh, qbn = qb;
+    if (Ln >= 0) decode(Ln, bhn, qbn);
+    const size_t hoffn = (size_t)bhn * N * D;
+    // step that copies the next Q block into qs: after at least one barrier
+    // has followed the Q fragment reads above
+    const int tq = nt >= 2 ? max(1, nt - 2) : 0;
+    if (nt == 1) ring_barrier();
+    // step t reads stage S and copies into the other one, which was last
+    // read in step t-1 (barrier since)
+    auto step = [&](int t, auto S) {
+      constexpr int SN = 1 - decltype(S)::value;
+      if (t + 1 < nt) {
+        dma_tile<D, BC, C::NT>(rk, (t + 1) * BC, kst(std::integral_constant<int, SN>{}), tid);
+        dma_tile<D, BC, C::NT>(rv, (t + 1) * BC, vst(std::integral_constant<int, SN>{}), tid);
+      } else if (Ln >= 0) {
+        keep_branch();
+        dma_tile<D, BC, C::NT>(make_copy_rsrc(K + hoffn, head_bytes), 0,
+                               kst(std::integral_constant<int, SN>{}), tid);
+        dma_tile<D, BC, C::NT>(make_copy_rsrc(V + hoffn, head_bytes), 0,
+                               vst(std::integral_constant<int, SN>{}), tid);
+      }
+      const bool qcopy = t == tq && Ln >= 0;
+      if (qcopy) {
+        keep_branch();
+        dma_tile<D, C::BR, C::NT>(make_copy_rsrc(Q + hoffn, head_bytes), qbn * C::BR, qs, tid);
+      }
+      wv.block(t, t * BC, kst(S), vst(S), bh, dr);
+      if (t + 1 < nt || Ln >= 0) {
+        // the next block must be resident; a Q copy issued after it may
+        // still be in flight unless this is the tile's last step
+        if (qcopy && t + 1 < nt) wait_vmem_le<QLOADS>();
+        else wait_vmem_all();
+        ring_barrier();
+      }
+    };
+    auto steps = [&](auto S0) {
+      constexpr int S1 = 1 - decltype(S0)::value;
+      for (int t0 = 0; t0 < nt; t0 += 2) {
+        step(t0, S0);
+        if (t0 + 1 < nt) step(t0 + 1, std::integral_constant<int, S1>{});
+      }
+    };
+    if (stage == 0) steps(std::integral_constant<int, 0>{});
+    else steps(std::integral_constant<int, 1>{});
+    stage ^= nt & 1;
+    wv.store(O + (size_t)bh * N * D, LSE + (size_t)bh * N, DROP ? dr.scale : 1.f);
+    if (Ln < 0) break;
+    bh = bhn;
+    qb = qbn;
+    rk = make_copy_rsrc(K + hoffn, head_bytes);
+    rv = make_copy_rsrc(V + hoffn, head_bytes);
   }
 }
 
@@ -505,14 +678,25 @@ hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* 
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = p.scale * kLog2e;
   const int G = head_group(OCC * 4 / NW, nqb);
-  if (sp.mask != nullptr)
+  if (sp.mask != nullptr) {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, true>), dim3((unsigned)grid),
                        dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                        (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, sp);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid),
-                       dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                       (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{});
+    return hipGetLastError();
+  }
+  if constexpr (C::QL && ST == 2 && kFwdPersistent) {
+    auto kern = fwd_bf16_persistent_kernel<D, NW, RB, BC, OCC, CAUSAL, false>;
+    const long long pg = persistent_grid(resident_workgroups(kern, C::NT), grid);
+    if (pg > 0) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)pg), dim3(C::NT), 0, stream, (const bf16_t*)Q,
+                         (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c,
+                         DropArgs{});
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid),
+                     dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                     (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{});
   return hipGetLastError();
 }
 
@@ -526,6 +710,15 @@ hipError_t run_fwd_drop(const void* Q, const void* K, const void* V, void* O, fl
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = p.scale * kLog2e;
   const int G = head_group(OCC * 4 / NW, nqb);
+  if constexpr (C::QL && ST == 2 && kFwdPersistent) {
+    auto kern = fwd_bf16_persistent_kernel<D, NW, RB, BC, OCC, CAUSAL, true>;
+    const long long pg = persistent_grid(resident_workgroups(kern, C::NT), grid);
+    if (pg > 0) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)pg), dim3(C::NT), 0, stream, (const bf16_t*)Q,
+                         (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c, dr);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, false, true>),
                      dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
                      (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{},
