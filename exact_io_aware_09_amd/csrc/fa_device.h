@@ -123,36 +123,6 @@ __device__ __forceinline__ void grouped_order(int L, int nblk, int BH, int G, in
   rank = r / gh;
 }
 
-// Persistent launches: the grid holds as many workgroups as the GPU keeps
-// resident at once, a multiple of the XCD count, and every workgroup loops
-// over tiles, prefetching the next tile's inputs while it computes the
-// current one (so the compulsory device-memory traffic of tile starts and
-// ends overlaps the matrix work instead of running between tiles).
-// Workgroup b runs on XCD b mod 8 and walks that XCD's contiguous range of
-// logical tiles (the same partition as xcd_remap) in rounds of one tile per
-// workgroup of the XCD, in snake order: position i in even rounds,
-// gx - 1 - i in odd ones.  Logical tiles come longest-first within a head
-// group (grouped_order), so over two rounds each workgroup takes one long
-// and one short causal tile.  Every tile of the range is visited exactly
-// once (each round is a permutation of the workgroup positions), the tile
-// index grows with the round, and -1 marks the end.
-struct PersistOrder {
-  int lo, cnt, gx, i;
-  __device__ __forceinline__ PersistOrder(int b, int grid, int total) {
-    const int x = b % kNumXcd;
-    i = b / kNumXcd;
-    gx = grid / kNumXcd;
-    const int q = total / kNumXcd, r = total % kNumXcd;
-    lo = x * q + (x < r ? x : r);
-    cnt = q + (x < r ? 1 : 0);
-  }
-  __device__ __forceinline__ int tile(int n) const {
-    const int pos = (n & 1) ? gx - 1 - i : i;
-    const long long j = (long long)n * gx + pos;
-    return j < cnt ? lo + (int)j : -1;
-  }
-};
-
 // Offsets of the blocks (BSZ rows or keys each, BSZ dividing 128) that a
 // workgroup visits in its main loop.  Dense: every block from `start` below
 // `end`.  Block-sparse: only the blocks inside the set 128 x 128 tiles of
@@ -308,12 +278,15 @@ typedef int copy_rsrc __attribute__((ext_vector_type(4)));  // buffer descriptor
 
 // Descriptor over `bytes` bytes at `base` (stride 0, raw buffer); reads at
 // or beyond `bytes` return zeros.  Same fields as make_rsrc.
+// The arguments are wave-uniform; the words are read from the first lane so
+// that the descriptor lives in SGPRs even where the compiler cannot prove
+// the uniformity itself.
 __device__ __forceinline__ copy_rsrc make_copy_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   copy_rsrc r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
-  r[2] = (int)bytes;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
   r[3] = 0x00020000;
   return r;
 }

@@ -50,12 +50,6 @@ namespace {
 
 constexpr float kMaxWeight = 65536.0f;  // bound on one lane's share of a block's row sum
 
-// Dense forwards whose Q blocks fit the LDS staging tile run persistent.
-#ifndef FA_FWD_PERSISTENT
-#define FA_FWD_PERSISTENT 1
-#endif
-constexpr bool kFwdPersistent = FA_FWD_PERSISTENT != 0;
-
 template <int D, int NW, int RB, int BC, int ST>
 struct FwdCfg {
   static constexpr int NT = NW * kWave;        // threads per workgroup
@@ -515,156 +509,37 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 
   if constexpr (!C::QL) {
     wv.store(O + hoff, LSE + (size_t)bh * N, DROP ? dr.scale : 1.f);
-    return;
-  }
-  // Epilogue through LDS: O = acc / l (bf16), LSE = m ln2 + ln l (fp32,
-  // natural log).
+  } else {
+    // Epilogue through LDS: O = acc / l (bf16), LSE = m ln2 + ln l (fp32,
+    // natural log).
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int query = q0w + 32 * rb + c32;
-    const float lt = sum_halves(wv.l[rb]);  // >= 1: the row maximum has weight >= 1
-    const float inv = DROP ? __builtin_amdgcn_rcpf(lt) * dr.scale : __builtin_amdgcn_rcpf(lt);
-    // O fragment (dims db*32 + 8g + 4h + 0..3 of this lane's row) into
-    // this wavefront's rows of the Q staging tile
+    for (int rb = 0; rb < RB; ++rb) {
+      const int query = q0w + 32 * rb + c32;
+      const float lt = sum_halves(wv.l[rb]);  // >= 1: the row maximum has weight >= 1
+      const float inv = DROP ? __builtin_amdgcn_rcpf(lt) * dr.scale : __builtin_amdgcn_rcpf(lt);
+      // O fragment (dims db*32 + 8g + 4h + 0..3 of this lane's row) into
+      // this wavefront's rows of the Q staging tile
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t lo = pack_bf16x2(wv.oacc[rb][db][4 * g] * inv, wv.oacc[rb][db][4 * g + 1] * inv);
-        const uint32_t hi = pack_bf16x2(wv.oacc[rb][db][4 * g + 2] * inv, wv.oacc[rb][db][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(qs + tile_off<D>(w * C::RW + 32 * rb + c32, db * 32 + 8 * g + 4 * h)) =
-            make_uint2(lo, hi);
-      }
-    if (h == 0 && query < N) LSE[(size_t)bh * N + query] = (wv.m[rb] + __builtin_amdgcn_logf(lt)) * kLn2;
-  }
-  // rows back out of LDS as whole 16-byte chunks: 8 lanes per row, so each
-  // store instruction writes 8 complete rows
-  constexpr int CPR = D / 8;
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t lo = pack_bf16x2(wv.oacc[rb][db][4 * g] * inv, wv.oacc[rb][db][4 * g + 1] * inv);
+          const uint32_t hi = pack_bf16x2(wv.oacc[rb][db][4 * g + 2] * inv, wv.oacc[rb][db][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(qs + tile_off<D>(w * C::RW + 32 * rb + c32, db * 32 + 8 * g + 4 * h)) =
+              make_uint2(lo, hi);
+        }
+      if (h == 0 && query < N) LSE[(size_t)bh * N + query] = (wv.m[rb] + __builtin_amdgcn_logf(lt)) * kLn2;
+    }
+    // rows back out of LDS as whole 16-byte chunks: 8 lanes per row, so each
+    // store instruction writes 8 complete rows
+    constexpr int CPR = D / 8;
 #pragma unroll
-  for (int i = 0; i < C::RW * CPR / kWave; ++i) {
-    const int chunk = i * kWave + lane;
-    const int r = chunk / CPR, cc = chunk % CPR;
-    const uint4 v = *reinterpret_cast<const uint4*>(qs + tile_off<D>(w * C::RW + r, cc * 8));
-    if (q0w + r < N) *reinterpret_cast<uint4*>(O + hoff + (size_t)(q0w + r) * D + cc * 8) = v;
-  }
-}
-
-// Persistent forward: gridDim.x workgroups (as many as stay resident) each
-// loop over query-block tiles in PersistOrder.  Two K/V stages; the K/V
-// ring runs on across tile boundaries (the last step of a tile copies the
-// first K/V block of the next tile, in the next tile's head), the next
-// tile's Q block is copied into the Q staging tile two steps before the end
-// (its rows are in registers by then), and O leaves straight from the
-// fragments, so a tile's inputs arrive and its outputs drain while the
-// matrix cores work.  The arithmetic of every tile is that of
-// fwd_bf16_kernel, so the results are bit for bit the same.
-template <int D, int NW, int RB, int BC, int OCC, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(NW * 64, OCC)
-void fwd_bf16_persistent_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
-                                const bf16_t* __restrict__ V, bf16_t* __restrict__ O,
-                                float* __restrict__ LSE, int BH, int N, int nqb, int G, float c,
-                                DropArgs dr) {
-  using C = FwdCfg<D, NW, RB, BC, 2>;
-  static_assert(C::QL, "the persistent forward stages Q blocks in LDS");
-  __shared__ __attribute__((aligned(16))) bf16_t k0s[C::TILE], v0s[C::TILE];
-  __shared__ __attribute__((aligned(16))) bf16_t k1s[C::TILE], v1s[C::TILE];
-  __shared__ __attribute__((aligned(16))) bf16_t qs[C::BR * D];
-  constexpr int QLOADS = C::BR * D / 8 / C::NT;  // Q-block copies per lane
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, uniform
-  const PersistOrder po(blockIdx.x, gridDim.x, BH * nqb);
-  int L = po.tile(0);
-  if (L < 0) return;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  auto decode = [&](int Lt, int& bh_, int& qb_) {
-    int rank;
-    grouped_order(Lt, nqb, BH, G, bh_, rank);
-    qb_ = CAUSAL ? (nqb - 1 - rank) : rank;  // longest causal blocks first
-  };
-  int bh, qb;
-  decode(L, bh, qb);
-  auto rk = make_copy_rsrc(K + (size_t)bh * N * D, head_bytes);
-  auto rv = make_copy_rsrc(V + (size_t)bh * N * D, head_bytes);
-  dma_tile<D, BC, C::NT>(rk, 0, k0s, tid);
-  dma_tile<D, BC, C::NT>(rv, 0, v0s, tid);
-  dma_tile<D, C::BR, C::NT>(make_copy_rsrc(Q + (size_t)bh * N * D, head_bytes), qb * C::BR, qs, tid);
-  wait_vmem_all();
-  ring_barrier();
-
-  FwdWave<D, NW, RB, BC, 2, CAUSAL, false, DROP> wv;
-  wv.N = N;
-  wv.lane = lane;
-  wv.h = lane >> 5;
-  wv.c32 = lane & 31;
-  wv.c = c;
-  auto kst = [&](auto S) -> bf16_t* {
-    if constexpr (decltype(S)::value == 0) return k0s;
-    else return k1s;
-  };
-  auto vst = [&](auto S) -> bf16_t* {
-    if constexpr (decltype(S)::value == 0) return v0s;
-    else return v1s;
-  };
-  int stage = 0;  // stage holding the tile's first K/V block
-  for (int n = 0;; ++n) {
-    const int q0 = qb * C::BR;
-    wv.q0w = q0 + w * C::RW;
-    wv.load_q(qs, w * C::RW);
-    wv.reset();
-    const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
-    const int nt = (kend + BC - 1) / BC;
-    const int Ln = po.tile(n + 1);
-    int bhn = bh, qbn = qb;
-    if (Ln >= 0) decode(Ln, bhn, qbn);
-    const size_t hoffn = (size_t)bhn * N * D;
-    // step that copies the next Q block into qs: after at least one barrier
-    // has followed the Q fragment reads above
-    const int tq = nt >= 2 ? max(1, nt - 2) : 0;
-    if (nt == 1) ring_barrier();
-    // step t reads stage S and copies into the other one, which was last
-    // read in step t-1 (barrier since)
-    auto step = [&](int t, auto S) {
-      constexpr int SN = 1 - decltype(S)::value;
-      if (t + 1 < nt) {
-        dma_tile<D, BC, C::NT>(rk, (t + 1) * BC, kst(std::integral_constant<int, SN>{}), tid);
-        dma_tile<D, BC, C::NT>(rv, (t + 1) * BC, vst(std::integral_constant<int, SN>{}), tid);
-      } else if (Ln >= 0) {
-        keep_branch();
-        dma_tile<D, BC, C::NT>(make_copy_rsrc(K + hoffn, head_bytes), 0,
-                               kst(std::integral_constant<int, SN>{}), tid);
-        dma_tile<D, BC, C::NT>(make_copy_rsrc(V + hoffn, head_bytes), 0,
-                               vst(std::integral_constant<int, SN>{}), tid);
-      }
-      const bool qcopy = t == tq && Ln >= 0;
-      if (qcopy) {
-        keep_branch();
-        dma_tile<D, C::BR, C::NT>(make_copy_rsrc(Q + hoffn, head_bytes), qbn * C::BR, qs, tid);
-      }
-      wv.block(t, t * BC, kst(S), vst(S), bh, dr);
-      if (t + 1 < nt || Ln >= 0) {
-        // the next block must be resident; a Q copy issued after it may
-        // still be in flight unless this is the tile's last step
-        if (qcopy && t + 1 < nt) wait_vmem_le<QLOADS>();
-        else wait_vmem_all();
-        ring_barrier();
-      }
-    };
-    auto steps = [&](auto S0) {
-      constexpr int S1 = 1 - decltype(S0)::value;
-      for (int t0 = 0; t0 < nt; t0 += 2) {
-        step(t0, S0);
-        if (t0 + 1 < nt) step(t0 + 1, std::integral_constant<int, S1>{});
-      }
-    };
-    if (stage == 0) steps(std::integral_constant<int, 0>{});
-    else steps(std::integral_constant<int, 1>{});
-    stage ^= nt & 1;
-    wv.store(O + (size_t)bh * N * D, LSE + (size_t)bh * N, DROP ? dr.scale : 1.f);
-    if (Ln < 0) break;
-    bh = bhn;
-    qb = qbn;
-    rk = make_copy_rsrc(K + hoffn, head_bytes);
-    rv = make_copy_rsrc(V + hoffn, head_bytes);
+    for (int i = 0; i < C::RW * CPR / kWave; ++i) {
+      const int chunk = i * kWave + lane;
+      const int r = chunk / CPR, cc = chunk % CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(qs + tile_off<D>(w * C::RW + r, cc * 8));
+      if (q0w + r < N) *reinterpret_cast<uint4*>(O + hoff + (size_t)(q0w + r) * D + cc * 8) = v;
+    }
   }
 }
 
@@ -678,25 +553,14 @@ hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* 
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = p.scale * kLog2e;
   const int G = head_group(OCC * 4 / NW, nqb);
-  if (sp.mask != nullptr) {
+  if (sp.mask != nullptr)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, true>), dim3((unsigned)grid),
                        dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                        (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, sp);
-    return hipGetLastError();
-  }
-  if constexpr (C::QL && ST == 2 && kFwdPersistent) {
-    auto kern = fwd_bf16_persistent_kernel<D, NW, RB, BC, OCC, CAUSAL, false>;
-    const long long pg = persistent_grid(resident_workgroups(kern, C::NT), grid);
-    if (pg > 0) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)pg), dim3(C::NT), 0, stream, (const bf16_t*)Q,
-                         (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c,
-                         DropArgs{});
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid),
-                     dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                     (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{});
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid),
+                       dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                       (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{});
   return hipGetLastError();
 }
 
@@ -710,15 +574,6 @@ hipError_t run_fwd_drop(const void* Q, const void* K, const void* V, void* O, fl
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = p.scale * kLog2e;
   const int G = head_group(OCC * 4 / NW, nqb);
-  if constexpr (C::QL && ST == 2 && kFwdPersistent) {
-    auto kern = fwd_bf16_persistent_kernel<D, NW, RB, BC, OCC, CAUSAL, true>;
-    const long long pg = persistent_grid(resident_workgroups(kern, C::NT), grid);
-    if (pg > 0) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)pg), dim3(C::NT), 0, stream, (const bf16_t*)Q,
-                         (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c, dr);
-      return hipGetLastError();
-    }
-  }
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, false, true>),
                      dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
                      (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{},

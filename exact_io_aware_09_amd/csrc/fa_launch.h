@@ -3,42 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <atomic>
-
 namespace fa {
-
-// Workgroups of `kernel` (with `threads` threads each) that the current
-// device keeps resident at once: compute units times the occupancy the
-// kernel's registers and LDS allow.  Queried once per device and kernel and
-// cached (the value never changes); 0 if the query fails.
-template <typename Kern>
-inline int resident_workgroups(Kern kernel, int threads) {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  int cus = 0, occ = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kernel),
-                                                   threads, 0) != hipSuccess)
-    return 0;
-  v = cus * occ;
-  if (v > 0) cache[dev].store(v, std::memory_order_relaxed);
-  return v;
-}
-
-// Grid of a persistent launch over `tiles` tiles: the resident workgroups,
-// rounded down to a multiple of the 8 XCDs, and no more than the tiles
-// need; 0 if the occupancy is unknown (the caller then launches one
-// workgroup per tile).
-inline long long persistent_grid(int resident, long long tiles) {
-  if (resident < 8 || tiles <= 0) return 0;
-  const long long per_xcd = (tiles + 7) / 8;
-  long long g = resident / 8;
-  if (g > per_xcd) g = per_xcd;
-  return 8 * g;
-}
 
 struct Problem {
   int B, H, N, d;
