@@ -87,10 +87,9 @@ struct DkdvCfg {
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int PU = BQ / 16;
-  // per stage and wavefront: Q and dO tiles (and, by wavefront 0 only in
-  // the copy modes that use one wavefront, the chunk's LSE*log2e and D)
+  // per stage and wavefront: Q and dO tiles, then one 4-byte copy each of
+  // the chunk's LSE*log2e and D
   static constexpr int DMA_PER_TILE = 2 * (TILE / 8 / NT) + 2;
-  static constexpr int DMA_PER_TILE_QO = 2 * (TILE / 8 / NT);
   // K and V blocks staged through LDS (coalesced copies in, dK and dV out
   // through the same rows) when both fit in 32 KB; otherwise their
   // fragments load straight from HBM
@@ -98,13 +97,6 @@ struct DkdvCfg {
   static_assert(BQ <= kWave, "one lane per chunk row copies LSE and D");
   static_assert(ST >= 2 && ST <= 3, "two or three Q/dO stages");
 };
-
-// How the dK/dV kernel stages each chunk's LSE*log2(e) and -D vectors:
-// 0 = every wavefront copies them buffer->LDS, 1 = wavefront 0 alone copies
-// them, 2 = wavefront 0 loads them into a register and stores them to LDS.
-#ifndef FA_DKDV_LD_MODE
-#define FA_DKDV_LD_MODE 0
-#endif
 
 // Per-wavefront state and per-chunk work of the dK/dV kernel: KB blocks of
 // 32 keys (first key k0w) whose K and V fragments stay in VGPRs (B operands
@@ -410,37 +402,13 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   auto fetch_at = [&](int i0, auto S) {
     dma_tile<D, C::BQ, C::NT>(rq, i0, qst(S), tid);
     dma_tile<D, C::BQ, C::NT>(ro, i0, ost(S), tid);
-    if constexpr (FA_DKDV_LD_MODE == 0) {
-      dma_rows_f32<C::BQ>(rl, i0, lst(S), lane);
-      dma_rows_f32<C::BQ>(rd, i0, dst_(S), lane);
-    } else if constexpr (FA_DKDV_LD_MODE == 1) {
-      if (w == 0) {
-        dma_rows_f32<C::BQ>(rl, i0, lst(S), lane);
-        dma_rows_f32<C::BQ>(rd, i0, dst_(S), lane);
-      }
-    }
+    dma_rows_f32<C::BQ>(rl, i0, lst(S), lane);
+    dma_rows_f32<C::BQ>(rd, i0, dst_(S), lane);
   };
   auto fetch = [&](int t, auto S) { fetch_at(qstart + t * C::BQ, S); };
-  // FA_DKDV_LD_MODE 2: wavefront 0 loads LSE*log2e (lanes 0..BQ-1) and -D
-  // (lanes 32..) of the next chunk into a register and stores it to the
-  // stage after the compute
-  const auto rlv = make_rsrc(Lws + (size_t)bh * N, (uint32_t)N * 4u);
-  const auto rdv = make_rsrc(Dws + (size_t)bh * N, (uint32_t)N * 4u);
-  auto ld_load = [&](int i0) -> float {
-    const int r = i0 + (lane & 31);
-    return lane < 32 ? buf_load_f32(rlv, (uint32_t)r * 4u) : buf_load_f32(rdv, (uint32_t)r * 4u);
-  };
-  auto ld_store = [&](float v, auto S) {
-    float* dst = lane < 32 ? lst(S) + lane : dst_(S) + (lane - 32);
-    *dst = v;
-  };
   // The first Q/dO copies go out before K and V are read, so that the
   // latencies overlap.
   if (ifirst >= 0) fetch_at(ifirst, std::integral_constant<int, 0>{});
-  if constexpr (FA_DKDV_LD_MODE == 2) {
-    static_assert(ST == 2 && C::BQ == 32, "register-staged LSE and D: two stages, 32-row chunks");
-    if (w == 0 && ifirst >= 0) ld_store(ld_load(ifirst), std::integral_constant<int, 0>{});
-  }
   if constexpr (C::KL) {
     // K and V blocks copied row-major (coalesced) into LDS, rows past N as 0
     dma_tile<D, C::BK, C::NT>(make_copy_rsrc(K + hoff, head_bytes), k0, ksg, tid);
@@ -484,23 +452,10 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     } else {
       if (t + ST - 1 < nchunks) fetch(t + ST - 1, std::integral_constant<int, SN>{});
     }
-    const int inext = SPARSE ? in : (t + 1 < nchunks ? i0 + C::BQ : -1);
-    float ldv = 0.f;
-    if constexpr (FA_DKDV_LD_MODE == 2) {
-      if (w == 0 && inext >= 0) ldv = ld_load(inext);
-    }
     wv.chunk(i0, qst(S), ost(S), lst(S), dst_(S), bh, dr);
-    if constexpr (FA_DKDV_LD_MODE == 2) {
-      if (w == 0 && inext >= 0) ld_store(ldv, std::integral_constant<int, SN>{});
-    }
     // step t+1 must be resident; later steps may still be in flight
     if (SPARSE ? in >= 0 : t + 1 < nchunks) {
-      if constexpr (FA_DKDV_LD_MODE == 0) {
-        wait_vmem_tiles<C::DMA_PER_TILE, ST - 2>(SPARSE ? 0 : min(ST - 2, nchunks - t - 2));
-      } else {
-        static_assert(FA_DKDV_LD_MODE == 0 || ST == 2, "one-wavefront LSE and D copies: two stages");
-        wait_vmem_all();
-      }
+      wait_vmem_tiles<C::DMA_PER_TILE, ST - 2>(SPARSE ? 0 : min(ST - 2, nchunks - t - 2));
       ring_barrier();
     }
   };

@@ -553,11 +553,15 @@ hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* 
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = p.scale * kLog2e;
   const int G = head_group(OCC * 4 / NW, nqb);
-  if (sp.mask != nullptr)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, true>), dim3((unsigned)grid),
-                       dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                       (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, sp);
-  else
+  if (sp.mask != nullptr) {
+    // the sparse walk takes 128-row query blocks in two stages
+    if constexpr (C::BR == 128 && ST == 2)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, true>), dim3((unsigned)grid),
+                         dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                         (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, sp);
+    else
+      return hipErrorNotSupported;
+  } else
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid),
                        dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                        (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{});
