@@ -60,6 +60,9 @@ def parse_args(argv=None):
                     help="time the FP8 forward (fa_forward_fp8) on inputs quantised beforehand "
                          "with fa_quantize_fp8; implies --fwd-only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-big-d", action="store_true",
+                    help="skip the head-dim-256 forward that the default run times beside the "
+                         "headline step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -174,6 +177,30 @@ def host_cpu() -> str:
     return "unknown"
 
 
+def host_cores() -> int:
+    """CPU cores this process may run on (its affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def blas_library() -> str:
+    """BLAS torch's CPU matrix products call, from torch's build configuration."""
+    import re
+
+    import torch
+
+    m = re.search(r"BLAS_INFO=([^,\s]+)", torch.__config__.show())
+    return m.group(1) if m else "unknown"
+
+
+def cpu_fields(threads_used: int):
+    """Host description reported beside the CPU baseline."""
+    return {"cores": host_cores(), "threads": threads_used, "blas": blas_library(),
+            "cpu_model": host_cpu()}
+
+
 def cpu_baseline_sampled(w, seconds: float):
     """Time the sampled-row oracle on query rows of the first head (N too large for S)."""
     import torch
@@ -196,8 +223,7 @@ def cpu_baseline_sampled(w, seconds: float):
     return {
         "value": tflops,
         "unit": "TFLOP/s",
-        "cores": torch.get_num_threads(),
-        "cpu_model": host_cpu(),
+        **cpu_fields(torch.get_num_threads()),
         "kind": "oracle",
         "sample": (f"fp64 sampled-row oracle (full score rows, O, LSE and dQ per row) on {done} "
                    f"query rows of head 0 of the {w.name} workload (N={w.N}, d={w.d}, "
@@ -233,13 +259,58 @@ def cpu_baseline(w, seconds: float):
     return {
         "value": tflops,
         "unit": "TFLOP/s",
-        "cores": torch.get_num_threads(),
-        "cpu_model": host_cpu(),
+        **cpu_fields(torch.get_num_threads()),
         "kind": "oracle",
         "sample": (f"fp64 oracle forward+backward (S, P materialised) on {heads_done} heads "
                    f"(N={w.N}, d={w.d}, causal={w.causal}) of the {w.name} workload's "
                    f"{w.B * w.H}; {t_used:.1f} s; credited FLOPs of those heads / time"),
     }
+
+
+def big_d_forward(steps: int = 10, warmup: int = 2):
+    """Forward throughput at head dim 256, long sequence (B 2, H 16, N 16384, d 256).
+
+    The second throughput target beside the headline step: fa_forward alone on
+    the workload's own seeded inputs, timed with HIP events on the launch
+    stream; credited FLOPs 4*B*H*N^2*d (non-causal).
+    """
+    import torch
+
+    from exact_io_aware_09_amd import _lib
+    from exact_io_aware_09_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS["big_d"]
+    B, H, N, d = w.shape
+    dev = torch.device("cuda:0")
+    q, k, v, _ = (t.to(dev) for t in make_inputs(w.shape, w.dtype, w.seed, w.mult))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    P = [t.data_ptr() for t in (q, k, v, o, lse)]
+
+    def run():
+        rc = _lib.fa_forward(*P, B, H, N, d, w.scale, int(w.causal), _lib.FA_BF16, stream.cuda_stream)
+        if rc != _lib.FA_OK:
+            raise _lib.FAError(rc, "fa_forward")
+
+    for _ in range(warmup):
+        run()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(steps):
+        run()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    ms = sum(ts) / steps
+    flops = 4 * B * H * N * N * d
+    tflops = flops / (ms * 1e-3) / 1e12
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+            "steps": steps, "ms": round(ms, 4), "ms_median": round(ts[len(ts) // 2], 4),
+            "tflops": round(tflops, 2), "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2)}
 
 
 def calibrate_copy():
@@ -461,6 +532,10 @@ def main(argv=None):
         },
         "cpu_baseline": None,
     }
+    default_run = (args.workload == "gpt2_medium" and not args.fwd_only and not fused
+                   and args.splits == 1 and not args.fp8)
+    if default_run and not args.no_big_d:
+        result["big_d_fwd"] = big_d_forward()
     if not args.no_cpu_baseline and not fused and args.splits == 1 and not args.fp8:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -25,6 +25,20 @@ def _check(name, t, ref=None):
             raise ValueError(f"{name} must match Q in shape, dtype and device")
 
 
+def _check_lse(lse, q):
+    B, H, N = q.shape[:3]
+    if (not isinstance(lse, torch.Tensor) or lse.shape != (B, H, N) or lse.dtype != torch.float32
+            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on the inputs' device")
+
+
+def _check_workspace(ws, need, q):
+    if (not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or not ws.is_contiguous()
+            or ws.device != q.device or ws.numel() < need):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {need} bytes "
+                         "on the inputs' device")
+
+
 def _dims(q):
     if q.dim() != 4:
         raise ValueError("expected [B, H, N, d] tensors")
@@ -46,6 +60,7 @@ def forward(q, k, v, scale: float, causal: bool = False, out=None, lse=None):
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check("out", o, q)
+    _check_lse(lse_t, q)
     rc = _lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                          lse_t.data_ptr(), B, H, N, d, scale, int(bool(causal)), dt,
                          _stream(q.device))
@@ -64,8 +79,10 @@ def forward_split(q, k, v, scale: float, causal: bool = False, splits: int = 2, 
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check("out", o, q)
+    _check_lse(lse_t, q)
     need = _lib.fa_forward_split_workspace_bytes(B, H, N, d, splits, dt)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    _check_workspace(ws, need, q)
     rc = _lib.fa_forward_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                lse_t.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                                B, H, N, d, scale, int(bool(causal)), splits, dt, _stream(q.device))
@@ -121,6 +138,7 @@ def backward_sparse(q, k, v, o, do, lse, block_mask, scale: float, causal: bool 
         _check(name, t, None if name == "q" else q)
     B, H, N, d, dt = _dims(q)
     _mask_check(block_mask, q)
+    _check_lse(lse, q)
     ws = torch.empty(_lib.fa_backward_workspace_bytes(B, H, N, d, dt), dtype=torch.uint8,
                      device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
@@ -155,8 +173,7 @@ def backward_dropout(q, k, v, o, do, lse, scale: float, causal: bool, p_drop: fl
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check(name, t, None if name == "q" else q)
     B, H, N, d, dt = _dims(q)
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    _check_lse(lse, q)
     ws = torch.empty(_lib.fa_backward_workspace_bytes(B, H, N, d, dt), dtype=torch.uint8,
                      device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
@@ -227,13 +244,15 @@ def backward(q, k, v, o, do, lse, scale: float, causal: bool = False, workspace=
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check(name, t, None if name == "q" else q)
     B, H, N, d, dt = _dims(q)
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    _check_lse(lse, q)
     need = _lib.fa_backward_workspace_bytes(B, H, N, d, dt)
     ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    _check_workspace(ws, need, q)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, q)
     rc = _lib.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                           do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                           dv.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),

@@ -945,32 +945,40 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
 #define FA_BWD_CFG_D256 4, 1, 1, 2, 1, 4, 1, 32, 2, 1
 #endif
 
+// All variants (dropout, block-sparse, plain) for one value of the causal
+// flag.
+template <int D, int NWK, int KBK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ,
+          int OCCQ, bool CAUSAL>
+hipError_t run_bwd_cz(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* LSE, void* dQ, void* dK, void* dV, float* ws, const Problem& p,
+                      unsigned stages, SparseArgs sp, hipStream_t stream, const DropArgs* dr) {
+  if (dr != nullptr) {
+    if (sp.mask != nullptr) return hipErrorNotSupported;
+    return run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, CAUSAL, false, true>(
+        Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream, *dr);
+  }
+  if (sp.mask != nullptr) {
+    // the sparse walk takes 128-key and 128-row blocks in two stages
+    if constexpr (NWK * KBK * 32 == 128 && STK == 2 && NWQ * RBQ * 32 == 128 && STQ == 2)
+      return run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, CAUSAL, true>(
+          Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream);
+    else
+      return hipErrorNotSupported;
+  }
+  return run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, CAUSAL, false>(
+      Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream);
+}
+
 template <int D, int NWK, int KBK, int QB, int STK, int OCCK, int NWQ, int RBQ, int BC, int STQ,
           int OCCQ>
 hipError_t run_bwd_c(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                      const float* LSE, void* dQ, void* dK, void* dV, float* ws, const Problem& p,
                      unsigned stages, SparseArgs sp, hipStream_t stream, const DropArgs* dr) {
-  if (dr != nullptr) {
-    if (sp.mask != nullptr) return hipErrorNotSupported;
-    return p.causal ? run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true, false, true>(
-                          Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream, *dr)
-                    : run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false, false, true>(
-                          Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream, *dr);
-  }
-  if (sp.mask != nullptr) {
-    // the sparse walk takes 128-key and 128-row blocks in two stages
-    if constexpr (NWK * KBK * 32 == 128 && STK == 2 && NWQ * RBQ * 32 == 128 && STQ == 2)
-      return p.causal ? run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true, true>(
-                            Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream)
-                      : run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false, true>(
-                            Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream);
-    else
-      return hipErrorNotSupported;
-  }
-  return p.causal ? run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true, false>(
-                        Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream)
-                  : run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false, false>(
-                        Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream);
+  return p.causal
+             ? run_bwd_cz<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, true>(
+                   Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream, dr)
+             : run_bwd_cz<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, false>(
+                   Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream, dr);
 }
 
 }  // namespace
@@ -1000,7 +1008,9 @@ hipError_t launch_backward_bf16_d128nc(const void* Q, const void* K, const void*
                                        const void* dO, const float* LSE, void* dQ, void* dK,
                                        void* dV, float* Dws, const Problem& p, unsigned stages,
                                        hipStream_t stream, SparseArgs sp, const DropArgs* dr) {
-  return run_bwd_c<128, FA_BWD_CFG_D128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp, stream, dr);
+  if (p.causal) return hipErrorInvalidValue;
+  return run_bwd_cz<128, FA_BWD_CFG_D128, false>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, stages, sp,
+                                                 stream, dr);
 }
 #else
 // Head dim 256 (this source compiled a second time as fa_bwd_d256.hip)

@@ -1,11 +1,12 @@
-"""Register budget of the head-dim-256 kernels (compile-only, no GPU).
+"""Register budget of the one-wavefront-per-SIMD kernels (compile-only, no GPU).
 
-The head-dim-256 kernels run one wavefront per SIMD; their speed depends on
-the matrix instructions keeping their accumulators in VGPRs (the units
-fa_*_d256.hip are built that way) and on no register being spilled to
+The head-dim-256 kernels, and the non-causal head-dim-128 dK/dV kernels, run
+one wavefront per SIMD; their speed depends on the matrix instructions
+keeping their accumulators in VGPRs (the units fa_*_d256.hip and
+fa_bwd_d128nc.hip are built that way) and on no register being spilled to
 scratch memory.  This compiles those units for gfx950 with the compiler's
-resource-usage remarks and checks every kernel in them: scratch 0 bytes per
-lane.  A toolchain or source change that brings spills back fails here.
+resource-usage remarks and checks their kernels: scratch 0 bytes per lane.
+A toolchain or source change that brings spills back fails here.
 """
 import re
 import shutil
@@ -17,6 +18,7 @@ import pytest
 from exact_io_aware_09_amd import build as B
 
 D256_UNITS = [(n, f) for n, f in B.UNITS if n.endswith("_d256.hip")]
+D128NC_UNIT = [(n, f) for n, f in B.UNITS if n == "fa_bwd_d128nc.hip"]
 
 
 def resource_remarks(name, extra):
@@ -49,3 +51,24 @@ def test_head_dim_256_kernels_do_not_spill():
                 continue
             assert r.get("ScratchSize [bytes/lane]") == 0, f"{name}: {k} spills ({r})"
             assert r["VGPRs"] + r.get("AGPRs", 0) <= 512, f"{name}: {k} {r}"
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not (B.Path("/opt/rocm/bin/hipcc").exists()),
+                    reason="hipcc not available")
+def test_head_dim_128_noncausal_unit():
+    # the unit holds only non-causal kernels (its launcher refuses causal
+    # problems), and its dK/dV kernels -- plain, dropout and block-sparse --
+    # and the plain and block-sparse dQ kernels spill nothing
+    (name, extra), = D128NC_UNIT
+    kernels = resource_remarks(name, extra)
+    assert kernels, f"{name}: no kernels reported"
+    dkdv = [k for k in kernels if "bwd_dkdv_bf16_kernelILi128E" in k]
+    dq = [k for k in kernels if "bwd_dq_bf16_kernelILi128E" in k]
+    assert len(dkdv) == 3 and len(dq) == 3, sorted(kernels)
+    for k in dkdv + dq:
+        # template arguments after the launch configuration: causal, sparse, dropout
+        flags = re.search(r"ELb([01])ELb([01])ELb([01])E", k)
+        assert flags and flags.group(1) == "0", f"causal kernel compiled in {name}: {k}"
+        if k in dq and flags.group(3) == "1":
+            continue  # the dropout dQ keeps a few bytes of spill (not on a measured path)
+        assert kernels[k].get("ScratchSize [bytes/lane]") == 0, f"{name}: {k} spills ({kernels[k]})"

@@ -44,3 +44,44 @@ def test_readme_example_runs():
     for name in ("q", "k", "v"):
         assert ns[name].shape == (2, 16, 1024, 64)
     assert torch.isfinite(ns["o"].float()).all() and torch.isfinite(ns["dq"].float()).all()
+
+
+def test_wrappers_reject_wrong_caller_buffers():
+    # every caller-supplied buffer is checked on the host before any launch
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in make_inputs((1, 2, 96, 64), torch.bfloat16, 5))
+    o, lse = fa.forward(q, k, v, 0.125, True)
+    bad_lse = (torch.empty((1, 2, 95), dtype=torch.float32, device=dev),
+               torch.empty((1, 2, 96), dtype=torch.bfloat16, device=dev),
+               torch.empty((1, 2, 96, 2), dtype=torch.float32, device=dev)[..., 0])
+    for b in bad_lse:
+        with pytest.raises(ValueError):
+            fa.forward(q, k, v, 0.125, True, lse=b)
+        with pytest.raises(ValueError):
+            fa.forward_split(q, k, v, 0.125, True, splits=2, lse=b)
+        with pytest.raises(ValueError):
+            fa.backward(q, k, v, o, do, b, 0.125, True)
+        with pytest.raises(ValueError):
+            fa.backward_sparse(q, k, v, o, do, b, torch.ones((1, 1), dtype=torch.int32, device=dev),
+                               0.125, True)
+    for name in ("dq", "dk", "dv"):
+        with pytest.raises(ValueError):
+            fa.backward(q, k, v, o, do, lse, 0.125, True, **{name: torch.empty_like(q)[:, :, :95]})
+        with pytest.raises(ValueError):
+            fa.backward(q, k, v, o, do, lse, 0.125, True, **{name: torch.empty_like(q, dtype=torch.float32)})
+    need = fa.workspace_bytes(1, 2, 96, 64, torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.backward(q, k, v, o, do, lse, 0.125, True,
+                    workspace=torch.empty(need - 1, dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError):
+        fa.backward(q, k, v, o, do, lse, 0.125, True,
+                    workspace=torch.empty(need, dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        fa.forward_split(q, k, v, 0.125, True, splits=2,
+                         workspace=torch.empty(16, dtype=torch.uint8, device=dev))
+    # the right buffers still work
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    dq = torch.empty_like(q)
+    got = fa.backward(q, k, v, o, do, lse, 0.125, True, workspace=ws, dq=dq)
+    torch.cuda.synchronize()
+    assert got[0] is dq
