@@ -98,222 +98,6 @@ struct DkdvCfg {
   static_assert(ST >= 2 && ST <= 3, "two or three Q/dO stages");
 };
 
-// Per-wavefront state and per-chunk work of the dK/dV kernel: KB blocks of
-// 32 keys (first key k0w) whose K and V fragments stay in VGPRs (B operands
-// of S = Q K^T and dP = dO V^T, lane = key), and the dK^T, dV^T
-// accumulators (lane = key; registers: head dims).
-template <int D, int NW, int KB, int QB, int ST, bool CAUSAL, bool DROP, int PARTS>
-struct DkdvWave {
-  using C = DkdvCfg<D, NW, KB, QB, ST>;
-  static constexpr bool DVP = PARTS & 1, DKP = PARTS & 2;
-  bf16x8 kf[KB][C::KSTEPS], vf[KB][C::KSTEPS];
-  f32x16 dkacc[KB][C::DB], dvacc[KB][C::DB];
-  int k0w, N, lane, h, c32;
-  float c;
-
-  __device__ __forceinline__ void reset() {
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          dkacc[kk][db][r] = 0.f;
-          dvacc[kk][db][r] = 0.f;
-        }
-  }
-
-  // K and V fragments of this wavefront's keys from row-major staging tiles
-  // (row 0 of the tiles = key k0w - row0).
-  __device__ __forceinline__ void load_kv(const bf16_t* ks, const bf16_t* vs, int row0) {
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
-        kf[kk][s] = frag_rows<D>(ks, row0 + 32 * kk, 16 * s, c32, h);
-        if constexpr (DKP) vf[kk][s] = frag_rows<D>(vs, row0 + 32 * kk, 16 * s, c32, h);
-      }
-  }
-
-  // The query chunk at row i0 (Q, dO tiles and its LSE*log2(e), -D vectors
-  // staged in LDS).
-  __device__ __forceinline__ void chunk(int i0, const bf16_t* Qs, const bf16_t* Os, const float* ls,
-                                        const float* ds, int bh, const DropArgs& dr) {
-    // some query of the chunk sees some key of this wavefront
-    const bool active = !CAUSAL || i0 + C::BQ - 1 >= k0w;
-    if (!active) return;
-
-    // S = Q K^T and dP - D = dO V^T - D (lane: key; registers: query
-    // rows); the dP accumulator starts from the workspace's -D, register
-    // 4g + e holding row 8g + 4h + e of the block (16-byte LDS reads).
-    f32x16 sacc[QB][KB], pacc[QB][KB];
-    f32x16 ndq[DROP ? QB : 1];  // DROP: -D t/256, the dS factor of dropped pairs
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 nd = {};
-      if constexpr (DKP) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(ds + qb * 32 + 8 * g + 4 * h);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) nd[4 * g + e] = DROP ? v[e] * dr.keep : v[e];
-        }
-      }
-      if constexpr (DROP) ndq[qb] = nd;
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
-        const bf16x8 aq = frag_rows<D>(Qs, qb * 32, 16 * s, c32, h);
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk) {
-          const f32x16 z = {};
-          sacc[qb][kk] = mfma32x32x16(aq, kf[kk][s], s == 0 ? z : sacc[qb][kk]);
-        }
-        if constexpr (DKP) {
-          const bf16x8 ao = frag_rows<D>(Os, qb * 32, 16 * s, c32, h);
-#pragma unroll
-          for (int kk = 0; kk < KB; ++kk)
-            pacc[qb][kk] = mfma32x32x16(ao, vf[kk][s], s == 0 ? nd : pacc[qb][kk]);
-        }
-      }
-    }
-
-    // P = exp2(S c - LSE2), in place; masked entries (causal future, query
-    // tail) are zeroed on the blocks that need it only (a real branch).
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // rows 8g + 4h + 0..3 of this 32-row block: one 16-byte LDS read
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * g + 4 * h);
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sacc[qb][kk][4 * g + e] = fast_exp2(fmaf(sacc[qb][kk][4 * g + e], c, -lse4[e]));
-      }
-    const bool tail = i0 + C::BQ > N;
-    if (tail || (CAUSAL && i0 < k0w + C::KW - 1)) {
-      keep_branch();
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        // key > query  <=>  kqh > query offset
-        const int kqh = k0w + 32 * kk + c32 - i0 - 4 * h;
-        if (!tail) {
-          // causal diagonal only: one compare per entry
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
-              if (qoff < kqh) sacc[qb][kk][r] = 0.f;
-            }
-        } else {
-          const int nq = N - i0 - 4 * h;  // query >= N  <=>  query offset >= nq
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
-              if ((CAUSAL && kqh > qoff) || qoff >= nq) sacc[qb][kk][r] = 0.f;
-            }
-        }
-      }
-    }
-    // dS = P (dP - D); P and dS packed to bf16 as B operands (k-step
-    // u = 2*qb + (g>>1) holds registers 8*(g&1) .. of block qb).
-    if constexpr (DROP) {
-      // pacc becomes dS (up to 256/t): P (dP' - D t/256) for kept pairs,
-      // P (-D t/256) for dropped ones; sacc becomes Z P, the weights of dV
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          uint32_t dw[4];
-          draws_key_cols(i0 + 32 * qb, k0w + 32 * kk, bh, lane, dr.k0, dr.k1, dw);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool k = kept(dw, r, dr.thresh);
-            const float pv = sacc[qb][kk][r];
-            if constexpr (DKP) pacc[qb][kk][r] = pv * (k ? pacc[qb][kk][r] : ndq[qb][r]);
-            sacc[qb][kk][r] = k ? pv : 0.f;
-          }
-        }
-    }
-    uint32_t pw[KB][C::PU][4], sw[KB][C::PU][4];
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16& pr = sacc[qb][kk];
-          const int u = 2 * qb + (g >> 1), w0 = 2 * (g & 1);
-          if constexpr (DVP) {
-            pw[kk][u][w0] = pack_bf16x2(pr[4 * g], pr[4 * g + 1]);
-            pw[kk][u][w0 + 1] = pack_bf16x2(pr[4 * g + 2], pr[4 * g + 3]);
-          }
-          if constexpr (DKP) {
-            float dsv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              dsv[e] = DROP ? pacc[qb][kk][4 * g + e] : pr[4 * g + e] * pacc[qb][kk][4 * g + e];
-            sw[kk][u][w0] = pack_bf16x2(dsv[0], dsv[1]);
-            sw[kk][u][w0 + 1] = pack_bf16x2(dsv[2], dsv[3]);
-          }
-        }
-
-    // dV^T += dO^T P,  dK^T += Q^T dS  (lane: key; registers: head dims);
-    // each transposed Q / dO fragment feeds the KB key blocks.
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-      for (int u = 0; u < C::PU; ++u) {
-        if constexpr (DVP) {
-          const bf16x8 ao = frag_tr<D>(Os, 16 * u, db * 32, lane);
-#pragma unroll
-          for (int kk = 0; kk < KB; ++kk)
-            dvacc[kk][db] = mfma32x32x16(
-                ao, bf16x8_from(pw[kk][u][0], pw[kk][u][1], pw[kk][u][2], pw[kk][u][3]), dvacc[kk][db]);
-        }
-        if constexpr (DKP) {
-          const bf16x8 aq = frag_tr<D>(Qs, 16 * u, db * 32, lane);
-#pragma unroll
-          for (int kk = 0; kk < KB; ++kk)
-            dkacc[kk][db] = mfma32x32x16(
-                aq, bf16x8_from(sw[kk][u][0], sw[kk][u][1], sw[kk][u][2], sw[kk][u][3]), dkacc[kk][db]);
-        }
-      }
-    }
-  }
-
-  // dK = scale dK^T-acc^T, dV (bf16) straight from the fragments: each lane
-  // writes dims db*32 + 8g + 4h + 0..3 of its key rows.
-  __device__ __forceinline__ void store(bf16_t* dKh, bf16_t* dVh, float scale, float vscale) const {
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
-      const int key = k0w + 32 * kk + c32;
-      if (key < N) {
-        bf16_t* dKr = dKh + (size_t)key * D;
-        bf16_t* dVr = dVh + (size_t)key * D;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            bf16x4 vk, vv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              vk[e] = to_bf16(dkacc[kk][db][4 * g + e] * scale);
-              vv[e] = to_bf16(dvacc[kk][db][4 * g + e] * vscale);
-            }
-            const int col = db * 32 + 8 * g + 4 * h;
-            if constexpr (DKP) *reinterpret_cast<bf16x4*>(dKr + col) = vk;
-            if constexpr (DVP) *reinterpret_cast<bf16x4*>(dVr + col) = vv;
-          }
-      }
-    }
-  }
-};
-
 // SPARSE: block-sparse attention; the loop visits only the query chunks of
 // the 128 x 128 tiles set in column kb of the tile mask (the key block is
 // one tile column: BK = 128); with none, dK and dV are 0.
@@ -341,7 +125,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   static_assert(!(SPARSE && DROP), "one variant at a time");
   static_assert(!SPARSE || (ST == 2 && C::BK == 128), "sparse walk: two stages, 128-key blocks");
   static_assert(PARTS >= 1 && PARTS <= 3, "dV, dK or both");
-  constexpr bool DKP = PARTS & 2;
+  constexpr bool DVP = PARTS & 1, DKP = PARTS & 2;
   // per stage: Q tile, dO tile, and 64 floats each of LSE*log2e and D
   __shared__ __attribute__((aligned(16))) bf16_t q0s[C::TILE], o0s[C::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t q1s[C::TILE], o1s[C::TILE];
@@ -370,8 +154,7 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     else return d2s;
   };
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, uniform
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
   int bh, kb;  // causal: low key blocks see the most queries, run them first
   grouped_order(xcd_remap(blockIdx.x, BH * nkb), nkb, BH, G, bh, kb);
@@ -383,15 +166,18 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   const auto rd = make_copy_rsrc(Dws + (size_t)bh * N, (uint32_t)N * 4u);
 
   const int k0 = kb * C::BK;
-  DkdvWave<D, NW, KB, QB, ST, CAUSAL, DROP, PARTS> wv;
-  wv.k0w = k0 + w * C::KW;  // this lane's key rows: k0w + 32 kk + c32 (MFMA column)
-  wv.N = N;
-  wv.lane = lane;
-  wv.h = h;
-  wv.c32 = c32;
-  wv.c = c;
-  const int k0w = wv.k0w;
-  wv.reset();
+  const int k0w = k0 + w * C::KW;  // this lane's key rows: k0w + 32 kk + c32 (MFMA column)
+
+  f32x16 dkacc[KB][C::DB], dvacc[KB][C::DB];
+#pragma unroll
+  for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dkacc[kk][db][r] = 0.f;
+        dvacc[kk][db][r] = 0.f;
+      }
 
   const int qstart = CAUSAL ? (k0 / C::BQ) * C::BQ : 0;
   const int nchunks = (N - qstart + C::BQ - 1) / C::BQ;
@@ -409,6 +195,8 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   // The first Q/dO copies go out before K and V are read, so that the
   // latencies overlap.
   if (ifirst >= 0) fetch_at(ifirst, std::integral_constant<int, 0>{});
+  // K and V fragments: B operands of S = Q K^T and dP = dO V^T (lane = key).
+  bf16x8 kf[KB][C::KSTEPS], vf[KB][C::KSTEPS];
   if constexpr (C::KL) {
     // K and V blocks copied row-major (coalesced) into LDS, rows past N as 0
     dma_tile<D, C::BK, C::NT>(make_copy_rsrc(K + hoff, head_bytes), k0, ksg, tid);
@@ -421,8 +209,8 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         const uint32_t off = ((uint32_t)(k0w + 32 * kk + c32) * D + 16 * s + 8 * h) * 2u;
-        wv.kf[kk][s] = as_bf16x8(buf_load16(rk, off));
-        if constexpr (DKP) wv.vf[kk][s] = as_bf16x8(buf_load16(rv, off));
+        kf[kk][s] = as_bf16x8(buf_load16(rk, off));
+        if constexpr (DKP) vf[kk][s] = as_bf16x8(buf_load16(rv, off));
       }
     // K and V resident here: the compiler does not count the copies, so its
     // own waits for K and V must not fall inside the loop (where they would
@@ -431,8 +219,8 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
-        pin_ready(wv.kf[kk][s]);
-        if constexpr (DKP) pin_ready(wv.vf[kk][s]);
+        pin_ready(kf[kk][s]);
+        if constexpr (DKP) pin_ready(vf[kk][s]);
       }
   }
   if constexpr (ST > 2) {
@@ -440,8 +228,16 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   }
   wait_vmem_tiles<C::DMA_PER_TILE, ST - 2>(min(ST - 2, nchunks - 1));
   ring_barrier();
-  // each wavefront reads (and later overwrites with dK, dV) only its rows
-  if constexpr (C::KL) wv.load_kv(ksg, vsg, w * C::KW);
+  if constexpr (C::KL) {
+    // each wavefront reads (and later overwrites with dK, dV) only its rows
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        kf[kk][s] = frag_rows<D>(ksg, w * C::KW + 32 * kk, 16 * s, c32, h);
+        if constexpr (DKP) vf[kk][s] = frag_rows<D>(vsg, w * C::KW + 32 * kk, 16 * s, c32, h);
+      }
+  }
 
   // Step t on the chunk at query i0; in is the next chunk's query (SPARSE:
   // it is copied in during this step; -1 when this is the last).
@@ -452,7 +248,156 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     } else {
       if (t + ST - 1 < nchunks) fetch(t + ST - 1, std::integral_constant<int, SN>{});
     }
-    wv.chunk(i0, qst(S), ost(S), lst(S), dst_(S), bh, dr);
+    // some query of the chunk sees some key of this wavefront
+    const bool active = !CAUSAL || i0 + C::BQ - 1 >= k0w;
+    if (active) {
+      const bf16_t* Qs = qst(S);
+      const bf16_t* Os = ost(S);
+      const float* ls = lst(S);
+      const float* ds = dst_(S);
+
+      // S = Q K^T and dP - D = dO V^T - D (lane: key; registers: query
+      // rows); the dP accumulator starts from the workspace's -D, register
+      // 4g + e holding row 8g + 4h + e of the block (16-byte LDS reads).
+      f32x16 sacc[QB][KB], pacc[QB][KB];
+      f32x16 ndq[DROP ? QB : 1];  // DROP: -D t/256, the dS factor of dropped pairs
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x16 nd = {};
+        if constexpr (DKP) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(ds + qb * 32 + 8 * g + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nd[4 * g + e] = DROP ? v[e] * dr.keep : v[e];
+          }
+        }
+        if constexpr (DROP) ndq[qb] = nd;
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) {
+          const bf16x8 aq = frag_rows<D>(Qs, qb * 32, 16 * s, c32, h);
+#pragma unroll
+          for (int kk = 0; kk < KB; ++kk) {
+            const f32x16 z = {};
+            sacc[qb][kk] = mfma32x32x16(aq, kf[kk][s], s == 0 ? z : sacc[qb][kk]);
+          }
+          if constexpr (DKP) {
+            const bf16x8 ao = frag_rows<D>(Os, qb * 32, 16 * s, c32, h);
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+              pacc[qb][kk] = mfma32x32x16(ao, vf[kk][s], s == 0 ? nd : pacc[qb][kk]);
+          }
+        }
+      }
+
+      // P = exp2(S c - LSE2), in place; masked entries (causal future, query
+      // tail) are zeroed on the blocks that need it only (a real branch).
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // rows 8g + 4h + 0..3 of this 32-row block: one 16-byte LDS read
+          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * g + 4 * h);
+#pragma unroll
+          for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sacc[qb][kk][4 * g + e] = fast_exp2(fmaf(sacc[qb][kk][4 * g + e], c, -lse4[e]));
+        }
+      const bool tail = i0 + C::BQ > N;
+      if (tail || (CAUSAL && i0 < k0w + C::KW - 1)) {
+        keep_branch();
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+          // key > query  <=>  kqh > query offset
+          const int kqh = k0w + 32 * kk + c32 - i0 - 4 * h;
+          if (!tail) {
+            // causal diagonal only: one compare per entry
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
+                if (qoff < kqh) sacc[qb][kk][r] = 0.f;
+              }
+          } else {
+            const int nq = N - i0 - 4 * h;  // query >= N  <=>  query offset >= nq
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int qoff = qb * 32 + 8 * (r >> 2) + (r & 3);
+                if ((CAUSAL && kqh > qoff) || qoff >= nq) sacc[qb][kk][r] = 0.f;
+              }
+          }
+        }
+      }
+      // dS = P (dP - D); P and dS packed to bf16 as B operands (k-step
+      // u = 2*qb + (g>>1) holds registers 8*(g&1) .. of block qb).
+      if constexpr (DROP) {
+        // pacc becomes dS (up to 256/t): P (dP' - D t/256) for kept pairs,
+        // P (-D t/256) for dropped ones; sacc becomes Z P, the weights of dV
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            uint32_t dw[4];
+            draws_key_cols(i0 + 32 * qb, k0w + 32 * kk, bh, lane, dr.k0, dr.k1, dw);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const bool k = kept(dw, r, dr.thresh);
+              const float pv = sacc[qb][kk][r];
+              if constexpr (DKP) pacc[qb][kk][r] = pv * (k ? pacc[qb][kk][r] : ndq[qb][r]);
+              sacc[qb][kk][r] = k ? pv : 0.f;
+            }
+          }
+      }
+      uint32_t pw[KB][C::PU][4], sw[KB][C::PU][4];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& pr = sacc[qb][kk];
+            const int u = 2 * qb + (g >> 1), w0 = 2 * (g & 1);
+            if constexpr (DVP) {
+              pw[kk][u][w0] = pack_bf16x2(pr[4 * g], pr[4 * g + 1]);
+              pw[kk][u][w0 + 1] = pack_bf16x2(pr[4 * g + 2], pr[4 * g + 3]);
+            }
+            if constexpr (DKP) {
+              float dsv[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                dsv[e] = DROP ? pacc[qb][kk][4 * g + e] : pr[4 * g + e] * pacc[qb][kk][4 * g + e];
+              sw[kk][u][w0] = pack_bf16x2(dsv[0], dsv[1]);
+              sw[kk][u][w0 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+            }
+          }
+
+      // dV^T += dO^T P,  dK^T += Q^T dS  (lane: key; registers: head dims);
+      // each transposed Q / dO fragment feeds the KB key blocks.
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+        for (int u = 0; u < C::PU; ++u) {
+          if constexpr (DVP) {
+            const bf16x8 ao = frag_tr<D>(Os, 16 * u, db * 32, lane);
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+              dvacc[kk][db] = mfma32x32x16(
+                  ao, bf16x8_from(pw[kk][u][0], pw[kk][u][1], pw[kk][u][2], pw[kk][u][3]), dvacc[kk][db]);
+          }
+          if constexpr (DKP) {
+            const bf16x8 aq = frag_tr<D>(Qs, 16 * u, db * 32, lane);
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+              dkacc[kk][db] = mfma32x32x16(
+                  aq, bf16x8_from(sw[kk][u][0], sw[kk][u][1], sw[kk][u][2], sw[kk][u][3]), dkacc[kk][db]);
+          }
+        }
+      }
+    }
     // step t+1 must be resident; later steps may still be in flight
     if (SPARSE ? in >= 0 : t + 1 < nchunks) {
       wait_vmem_tiles<C::DMA_PER_TILE, ST - 2>(SPARSE ? 0 : min(ST - 2, nchunks - t - 2));
@@ -480,10 +425,15 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
     }
   }
 
-  const float vscale = DROP ? dr.scale : 1.f;
-  if constexpr (!C::KL) {
-    wv.store(dK + hoff, dV + hoff, scale, vscale);
-  } else {
+  if constexpr (DROP && DVP) {
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dvacc[kk][db][r] *= dr.scale;
+  }
+  if constexpr (C::KL) {
     // fragments (dims db*32 + 8g + 4h + 0..3 of this lane's key rows) into
     // this wavefront's rows of the staging tiles, then out as whole rows:
     // 8 lanes per row, each store instruction writes 8 complete rows
@@ -496,8 +446,8 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *reinterpret_cast<uint2*>(ksg + tile_off<D>(w * C::KW + 32 * kk + c32, db * 32 + 8 * g + 4 * h)) =
-              make_uint2(pack_bf16x2(wv.dkacc[kk][db][4 * g] * scale, wv.dkacc[kk][db][4 * g + 1] * scale),
-                         pack_bf16x2(wv.dkacc[kk][db][4 * g + 2] * scale, wv.dkacc[kk][db][4 * g + 3] * scale));
+              make_uint2(pack_bf16x2(dkacc[kk][db][4 * g] * scale, dkacc[kk][db][4 * g + 1] * scale),
+                         pack_bf16x2(dkacc[kk][db][4 * g + 2] * scale, dkacc[kk][db][4 * g + 3] * scale));
 #pragma unroll
     for (int i = 0; i < C::KW * CPR / kWave; ++i) {
       const int chunk = i * kWave + lane;
@@ -512,14 +462,37 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *reinterpret_cast<uint2*>(vsg + tile_off<D>(w * C::KW + 32 * kk + c32, db * 32 + 8 * g + 4 * h)) =
-              make_uint2(pack_bf16x2(wv.dvacc[kk][db][4 * g] * vscale, wv.dvacc[kk][db][4 * g + 1] * vscale),
-                         pack_bf16x2(wv.dvacc[kk][db][4 * g + 2] * vscale, wv.dvacc[kk][db][4 * g + 3] * vscale));
+              make_uint2(pack_bf16x2(dvacc[kk][db][4 * g], dvacc[kk][db][4 * g + 1]),
+                         pack_bf16x2(dvacc[kk][db][4 * g + 2], dvacc[kk][db][4 * g + 3]));
 #pragma unroll
     for (int i = 0; i < C::KW * CPR / kWave; ++i) {
       const int chunk = i * kWave + lane;
       const int r = chunk / CPR, cc = chunk % CPR;
       const uint4 v = *reinterpret_cast<const uint4*>(vsg + tile_off<D>(w * C::KW + r, cc * 8));
       if (k0w + r < N) *reinterpret_cast<uint4*>(dV + hoff + (size_t)(k0w + r) * D + cc * 8) = v;
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const int key = k0w + 32 * kk + c32;
+      if (key < N) {
+        bf16_t* dKr = dK + hoff + (size_t)key * D;
+        bf16_t* dVr = dV + hoff + (size_t)key * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 vk, vv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              vk[e] = to_bf16(dkacc[kk][db][4 * g + e] * scale);
+              vv[e] = to_bf16(dvacc[kk][db][4 * g + e]);
+            }
+            const int col = db * 32 + 8 * g + 4 * h;
+            if constexpr (DKP) *reinterpret_cast<bf16x4*>(dKr + col) = vk;
+            if constexpr (DVP) *reinterpret_cast<bf16x4*>(dVr + col) = vv;
+          }
+      }
     }
   }
 }

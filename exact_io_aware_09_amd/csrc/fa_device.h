@@ -278,15 +278,12 @@ typedef int copy_rsrc __attribute__((ext_vector_type(4)));  // buffer descriptor
 
 // Descriptor over `bytes` bytes at `base` (stride 0, raw buffer); reads at
 // or beyond `bytes` return zeros.  Same fields as make_rsrc.
-// The arguments are wave-uniform; the words are read from the first lane so
-// that the descriptor lives in SGPRs even where the compiler cannot prove
-// the uniformity itself.
 __device__ __forceinline__ copy_rsrc make_copy_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   copy_rsrc r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = (int)bytes;
   r[3] = 0x00020000;
   return r;
 }
@@ -324,61 +321,25 @@ __device__ __forceinline__ void lds_copy4(copy_rsrc r, uint32_t voff, uint32_t l
       : "memory");
 }
 
-// As lds_copy16, with the byte offset split into a per-lane part (VGPR) and
-// a part that is the same in every lane (SGPR; callers pass wave-uniform
-// values).
-__device__ __forceinline__ void lds_copy16_s(copy_rsrc r, uint32_t voff, uint32_t soff, uint32_t lds) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
-      : "memory");
-}
-
 // Copy of one [ROWS x D] bf16 block (rows r0.. of the descriptor's tensor)
 // into a swizzled LDS tile, without VGPRs.  Each wavefront instruction
 // writes 64 x 16 bytes to consecutive LDS addresses, so lane L fetches the
 // global chunk that the swizzle places at that position.  Rows past the end
 // of the descriptor read as zeros.  CHUNKS / NT copies per lane.
-// Head dim 64: a 1 KB block holds 8 rows and the swizzle repeats every 16
-// rows, so with an even number of wavefronts the blocks a wavefront writes
-// all start at the same phase of the swizzle (block w + i * NWAVE starts at
-// row 8 (w mod 2) mod 16).  Lane L then fetches the same chunk of its row
-// in every block: one per-lane byte offset for all the copies (and all
-// tiles of the kernel), the rest of the offset uniform (SGPR).
 template <int D, int ROWS, int NT>
 __device__ __forceinline__ void dma_tile(copy_rsrc r, int r0, bf16_t* tile, int tid) {
   constexpr int CPR = D / 8;               // chunks per row
   constexpr int CHUNKS = ROWS * CPR;
   constexpr int NWAVE = NT / kWave;
   static_assert(CHUNKS % NT == 0, "block must split evenly over the threads");
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if constexpr (D == 64 && NWAVE % 2 == 0) {
-    constexpr int RPB = kWave / CPR;       // rows per 1 KB block: 8
-    const int lrow = lane / CPR;
-    const int srow = ((w * RPB) & 15) + lrow;  // row within the swizzle's 16-row period
-    const uint32_t voff = (uint32_t)(lrow * D + ((lane % CPR) ^ swz<D>(srow)) * 8) * 2u;
+  const int w = tid >> 6, lane = tid & 63;
 #pragma unroll
-    for (int i = 0; i < CHUNKS / NT; ++i) {
-      const int blk = w + i * NWAVE;
-      const uint32_t soff = (uint32_t)(r0 + blk * RPB) * (D * 2u);
-      lds_copy16_s(r, voff, soff, lds_address(tile + blk * 512));
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < CHUNKS / NT; ++i) {
-      const int blk = w + i * NWAVE;           // 1 KB block of the tile written by this instruction
-      const int pos = blk * 64 + lane;         // chunk position in LDS
-      const int row = pos / CPR, c = (pos % CPR) ^ swz<D>(row);
-      const uint32_t goff = ((uint32_t)(r0 + row) * D + c * 8) * 2u;
-      lds_copy16(r, goff, lds_address(tile + blk * 512));
-    }
+  for (int i = 0; i < CHUNKS / NT; ++i) {
+    const int blk = w + i * NWAVE;           // 1 KB block of the tile written by this instruction
+    const int pos = blk * 64 + lane;         // chunk position in LDS
+    const int row = pos / CPR, c = (pos % CPR) ^ swz<D>(row);
+    const uint32_t goff = ((uint32_t)(r0 + row) * D + c * 8) * 2u;
+    lds_copy16(r, goff, lds_address(tile + blk * 512));
   }
 }
 

@@ -67,229 +67,11 @@ struct FwdCfg {
   static_assert(ST >= 2 && ST <= 3, "two or three K/V stages");
 };
 
-// Per-wavefront state and per-block work of the forward: RB blocks of 32
-// query rows (first row q0w), their Q fragments (B operands of S^T = K Q^T,
-// lane = query row), the running maximum m and row sum l of each row (the
-// lane's half of the row), and the unnormalised output O^T.  Every K and V
-// fragment read from LDS feeds the RB row blocks, which divides LDS reads
-// and HBM->LDS copies per FLOP by RB.
-template <int D, int NW, int RB, int BC, int ST, bool CAUSAL, bool SPLIT, bool DROP>
-struct FwdWave {
-  using C = FwdCfg<D, NW, RB, BC, ST>;
-  bf16x8 qf[RB][C::KSTEPS];
-  f32x16 oacc[RB][C::DB];
-  float m[RB], l[RB];
-  int q0w, N, lane, h, c32;
-  float c;
-
-  // Base of the exponent.  Every row sees key 0 of its first block, so m is
-  // finite -- except for a key range that starts after a causal row, which
-  // sees nothing of the range: its weights are then exp2(-inf) = 0.
-  __device__ __forceinline__ static float base(float mrow) {
-    return (SPLIT && CAUSAL && mrow == -INFINITY) ? 0.f : mrow;
-  }
-
-  __device__ __forceinline__ void reset() {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
-      m[rb] = -INFINITY;
-      l[rb] = 0.f;
-    }
-  }
-
-  // Q fragments of this wavefront's rows from a row-major staging tile
-  // (row 0 of the tile = query row q0w - row0).
-  __device__ __forceinline__ void load_q(const bf16_t* qs, int row0) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) qf[rb][s] = frag_rows<D>(qs, row0 + 32 * rb, 16 * s, c32, h);
-  }
-
-  // S^T = K Q^T for the block at key j0 (lane: query; registers: keys), each
-  // K fragment feeding the RB row blocks; causal-future keys and keys past
-  // the end become -inf, on the blocks that need it only.
-  __device__ __forceinline__ void scores(const bf16_t* Ks, int j0, f32x16 (&sacc)[RB][C::KB]) const {
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      bf16x8 kfr[C::KSTEPS];
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) kfr[s] = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
-      const f32x16 z = {};
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[0], qf[rb][0], z);
-#pragma unroll
-      for (int s = 1; s < C::KSTEPS; ++s)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[s], qf[rb][s], sacc[rb][kb]);
-    }
-    const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
-    if (need_mask) {
-      keep_branch();
-      const int nk = N - j0 - 4 * h;  // key >= N  <=>  key offset >= nk
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        // key - query = kq + key offset; future keys and keys past the end
-        // both have key offset > lim
-        const int kq = j0 + 4 * h - (q0w + 32 * rb + c32);
-        const int lim = CAUSAL ? min(-kq, nk - 1) : nk - 1;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
-            if (koff > lim) sacc[rb][kb][r] = -INFINITY;
-          }
-      }
-    }
-  }
-
-  // Row maximum of a block, scaled to log2 units (both halves of the row).
-  __device__ __forceinline__ float block_max(const f32x16 (&sacc)[C::KB]) const {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    return max_halves(mx) * c;
-  }
-
-  // P^T = exp2(c S^T - m) in place; returns this lane's share of the row sum.
-  __device__ __forceinline__ float exponentiate(f32x16 (&sacc)[C::KB], float mrow) const {
-    float part[C::KB * 8];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c, -mrow));
-        sacc[kb][r + 1] = fast_exp2(fmaf(sacc[kb][r + 1], c, -mrow));
-        part[kb * 8 + r / 2] = sacc[kb][r] + sacc[kb][r + 1];
-      }
-#pragma unroll
-    for (int n = C::KB * 8; n > 1; n /= 2)
-#pragma unroll
-      for (int i = 0; i < n / 2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
-    return part[0];
-  }
-
-  // The block at key j0, the t-th of this tile's walk (t = 0: first block):
-  // scores, online softmax, O^T += V^T P^T.
-  __device__ __forceinline__ void block(int t, int j0, const bf16_t* Ks, const bf16_t* Vs, int bh,
-                                        const DropArgs& dr) {
-    const bool active = !CAUSAL || j0 <= q0w + C::RW - 1;
-    if (!active) return;
-    f32x16 sacc[RB][C::KB];
-    scores(Ks, j0, sacc);
-    // Running maximum m (log2 units): taken from a row's first block
-    // (which always holds key 0, so it is finite) and afterwards kept
-    // while every exponentiated score of the row stays below kMaxWeight;
-    // numerator and denominator share the base, so O and the
-    // log-sum-exp do not depend on when m is raised.
-    if (t == 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) m[rb] = block_max(sacc[rb]);
-    }
-    float rs[RB];
-    bool over = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      rs[rb] = exponentiate(sacc[rb], base(m[rb]));
-      over |= !(rs[rb] <= kMaxWeight);
-    }
-    if (wave_any(over)) {
-      // Some row overflowed the bound: rows whose own share (either half)
-      // did so take the block's maximum, rescale O and l, and are
-      // exponentiated again; the other rows recompute the same values.
-      keep_branch();
-      f32x16 s2[RB][C::KB];
-      scores(Ks, j0, s2);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const bool own = !(rs[rb] <= kMaxWeight);
-        const bool row = max_halves(own ? 1.f : 0.f) > 0.f;
-        const float mx = block_max(s2[rb]);
-        if (row) {
-          const float alpha = fast_exp2(m[rb] - mx);
-          m[rb] = mx;
-          l[rb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
-        }
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) sacc[rb][kb] = s2[rb][kb];
-        rs[rb] = exponentiate(sacc[rb], base(m[rb]));
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) l[rb] += rs[rb];
-    if constexpr (DROP) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-          uint32_t dw[4];
-          draws_query_cols(q0w + 32 * rb, j0 + 32 * kb, bh, lane, dr.k0, dr.k1, dw);
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!kept(dw, r, dr.thresh)) sacc[rb][kb][r] = 0.f;
-        }
-    }
-
-    // P^T as B operand (k-step u: registers 8*(u&1).. of key block u>>1,
-    // i.e. keys 16u + 8*(e>>2) + 4h + (e&3)), rounded to bf16, then
-    // O^T += V^T P^T with each V fragment feeding the RB row blocks.
-#pragma unroll
-    for (int u = 0; u < C::PU; ++u) {
-      bf16x8 pf[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const f32x16& pv = sacc[rb][u >> 1];
-        const int r0 = 8 * (u & 1);
-        pf[rb] = bf16x8_from(pack_bf16x2(pv[r0], pv[r0 + 1]), pack_bf16x2(pv[r0 + 2], pv[r0 + 3]),
-                             pack_bf16x2(pv[r0 + 4], pv[r0 + 5]), pack_bf16x2(pv[r0 + 6], pv[r0 + 7]));
-      }
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 vfr = frag_tr<D>(Vs, 16 * u, db * 32, lane);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32x32x16(vfr, pf[rb], oacc[rb][db]);
-      }
-    }
-  }
-
-  // O = acc / l (bf16) straight from the fragments (dims db*32 + 8g + 4h +
-  // 0..3 of this lane's row) and LSE = m ln2 + ln l (fp32, natural log).
-  __device__ __forceinline__ void store(bf16_t* Oh, float* LSEh, float oscale) const {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int query = q0w + 32 * rb + c32;
-      const float lt = sum_halves(l[rb]);  // >= 1: the row maximum has weight >= 1
-      const float inv = __builtin_amdgcn_rcpf(lt) * oscale;
-      if (query < N) {
-        bf16_t* Or = Oh + (size_t)query * D;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const uint32_t lo = pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv);
-            const uint32_t hi = pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
-            *reinterpret_cast<uint2*>(Or + db * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
-          }
-        if (h == 0) LSEh[query] = (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2;
-      }
-    }
-  }
-};
-
-// One workgroup per query block (tile), loop over the K/V blocks of the
-// tile with the blocks of the next ST-1 steps in flight (direct
-// buffer->LDS loads).  A wavefront owns RB blocks of 32 query rows.
+// Per block t: S^T = K Q^T, mask, online softmax, O^T += V^T P^T, with the
+// K/V blocks of the next ST-1 steps in flight (direct buffer->LDS loads).
+// A wavefront owns RB blocks of 32 query rows: every K and V fragment read
+// from LDS feeds RB matrix instructions, which divides LDS reads and
+// HBM->LDS copies per FLOP by RB.
 //
 // SPLIT: the keys are cut into ranges of sa.span keys (a multiple of 64);
 // workgroup (tile, range) runs the loop over its range only and writes the
@@ -332,8 +114,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     else if constexpr (decltype(S)::value == 1) return v1s;
     else return v2s;
   };
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index, uniform
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
   int bh, rank, split = 0;
   if constexpr (SPLIT) {
@@ -351,14 +132,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   const auto rv = make_copy_rsrc(V + hoff, head_bytes);
 
   const int q0 = qb * C::BR;
-  FwdWave<D, NW, RB, BC, ST, CAUSAL, SPLIT, DROP> wv;
-  wv.q0w = q0 + w * C::RW;  // first query row of this wavefront
-  wv.N = N;
-  wv.lane = lane;
-  wv.h = h;
-  wv.c32 = c32;
-  wv.c = c;
-  const int q0w = wv.q0w;
+  const int q0w = q0 + w * C::RW;  // first query row of this wavefront
   // this lane's query row in row block rb is q0w + 32 * rb + c32
 
   // keys [kbase, kend) of this workgroup: blocks kbase + t*BC, t < ntiles
@@ -414,6 +188,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   // The first K/V copies go out before Q is read, so that the latencies
   // overlap.
   fetch_at(jfirst, std::integral_constant<int, 0>{});
+  bf16x8 qf[RB][C::KSTEPS];  // B operands of S^T = K Q^T (lane = query row)
   if constexpr (C::QL) {
     // Q block copied row-major (coalesced) into LDS, rows past N as zeros
     dma_tile<D, C::BR, C::NT>(make_copy_rsrc(Q + hoff, head_bytes), q0, qs, tid);
@@ -423,7 +198,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s)
-        wv.qf[rb][s] = as_bf16x8(
+        qf[rb][s] = as_bf16x8(
             buf_load16(rq, ((uint32_t)(q0w + 32 * rb + c32) * D + 16 * s + 8 * h) * 2u));
     // Q resident here: the compiler does not count the copies, so its own
     // waits for Q must not fall inside the loop (where they would also
@@ -431,16 +206,101 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) pin_ready(wv.qf[rb][s]);
+      for (int s = 0; s < C::KSTEPS; ++s) pin_ready(qf[rb][s]);
   }
   if constexpr (ST > 2) {
     if (1 < ntiles) fetch(1, std::integral_constant<int, 1>{});
   }
   wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - 1));
   ring_barrier();
-  // each wavefront reads (and later overwrites with O) only its own rows
-  if constexpr (C::QL) wv.load_q(qs, w * C::RW);
-  wv.reset();
+  if constexpr (C::QL) {
+    // each wavefront reads (and later overwrites with O) only its own rows
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s)
+        qf[rb][s] = frag_rows<D>(qs, w * C::RW + 32 * rb, 16 * s, c32, h);
+  }
+
+  f32x16 oacc[RB][C::DB];
+  float m[RB], l[RB];
+  // Base of the exponent.  Every row sees key 0 of its first block, so m is
+  // finite -- except for a key range that starts after a causal row, which
+  // sees nothing of the range: its weights are then exp2(-inf) = 0.
+  auto base = [](float mrow) { return (SPLIT && CAUSAL && mrow == -INFINITY) ? 0.f : mrow; };
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+  }
+
+  // S^T = K Q^T for the block at key j0 (lane: query; registers: keys), each
+  // K fragment feeding the RB row blocks; causal-future keys and keys past
+  // the end become -inf, on the blocks that need it only.
+  auto scores = [&](const bf16_t* Ks, int j0, f32x16 (&sacc)[RB][C::KB]) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      bf16x8 kfr[C::KSTEPS];
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) kfr[s] = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
+      const f32x16 z = {};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[0], qf[rb][0], z);
+#pragma unroll
+      for (int s = 1; s < C::KSTEPS; ++s)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[s], qf[rb][s], sacc[rb][kb]);
+    }
+    const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
+    if (need_mask) {
+      keep_branch();
+      const int nk = N - j0 - 4 * h;  // key >= N  <=>  key offset >= nk
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        // key - query = kq + key offset; future keys and keys past the end
+        // both have key offset > lim
+        const int kq = j0 + 4 * h - (q0w + 32 * rb + c32);
+        const int lim = CAUSAL ? min(-kq, nk - 1) : nk - 1;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
+            if (koff > lim) sacc[rb][kb][r] = -INFINITY;
+          }
+      }
+    }
+  };
+  // Row maximum of a block, scaled to log2 units (both halves of the row).
+  auto block_max = [&](const f32x16 (&sacc)[C::KB]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    return max_halves(mx) * c;
+  };
+  // P^T = exp2(c S^T - m) in place; returns this lane's share of the row sum.
+  auto exponentiate = [&](f32x16 (&sacc)[C::KB], float mrow) {
+    float part[C::KB * 8];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c, -mrow));
+        sacc[kb][r + 1] = fast_exp2(fmaf(sacc[kb][r + 1], c, -mrow));
+        part[kb * 8 + r / 2] = sacc[kb][r] + sacc[kb][r + 1];
+      }
+#pragma unroll
+    for (int n = C::KB * 8; n > 1; n /= 2)
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
+    return part[0];
+  };
 
   // Step t on the block at key j0; jn is the next block's key (SPARSE: it
   // is copied in during this step; -1 when this is the last).
@@ -452,7 +312,90 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     } else {
       if (t + ST - 1 < ntiles) fetch(t + ST - 1, std::integral_constant<int, SN>{});
     }
-    wv.block(t, j0, kst(S), vst(S), bh, dr);
+    const bool active = !CAUSAL || j0 <= q0w + C::RW - 1;
+    if (active) {
+      const bf16_t* Ks = kst(S);
+      const bf16_t* Vs = vst(S);
+      f32x16 sacc[RB][C::KB];
+      scores(Ks, j0, sacc);
+      // Running maximum m (log2 units): taken from a row's first block
+      // (which always holds key 0, so it is finite) and afterwards kept
+      // while every exponentiated score of the row stays below kMaxWeight;
+      // numerator and denominator share the base, so O and the
+      // log-sum-exp do not depend on when m is raised.
+      if (t == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) m[rb] = block_max(sacc[rb]);
+      }
+      float rs[RB];
+      bool over = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        rs[rb] = exponentiate(sacc[rb], base(m[rb]));
+        over |= !(rs[rb] <= kMaxWeight);
+      }
+      if (wave_any(over)) {
+        // Some row overflowed the bound: rows whose own share (either half)
+        // did so take the block's maximum, rescale O and l, and are
+        // exponentiated again; the other rows recompute the same values.
+        keep_branch();
+        f32x16 s2[RB][C::KB];
+        scores(Ks, j0, s2);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const bool own = !(rs[rb] <= kMaxWeight);
+          const bool row = max_halves(own ? 1.f : 0.f) > 0.f;
+          const float mx = block_max(s2[rb]);
+          if (row) {
+            const float alpha = fast_exp2(m[rb] - mx);
+            m[rb] = mx;
+            l[rb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+          }
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb) sacc[rb][kb] = s2[rb][kb];
+          rs[rb] = exponentiate(sacc[rb], base(m[rb]));
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) l[rb] += rs[rb];
+      if constexpr (DROP) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb) {
+            uint32_t dw[4];
+            draws_query_cols(q0w + 32 * rb, j0 + 32 * kb, bh, lane, dr.k0, dr.k1, dw);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (!kept(dw, r, dr.thresh)) sacc[rb][kb][r] = 0.f;
+          }
+      }
+
+      // P^T as B operand (k-step u: registers 8*(u&1).. of key block u>>1,
+      // i.e. keys 16u + 8*(e>>2) + 4h + (e&3)), rounded to bf16, then
+      // O^T += V^T P^T with each V fragment feeding the RB row blocks.
+#pragma unroll
+      for (int u = 0; u < C::PU; ++u) {
+        bf16x8 pf[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const f32x16& pv = sacc[rb][u >> 1];
+          const int r0 = 8 * (u & 1);
+          pf[rb] = bf16x8_from(pack_bf16x2(pv[r0], pv[r0 + 1]), pack_bf16x2(pv[r0 + 2], pv[r0 + 3]),
+                               pack_bf16x2(pv[r0 + 4], pv[r0 + 5]), pack_bf16x2(pv[r0 + 6], pv[r0 + 7]));
+        }
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x8 vfr = frag_tr<D>(Vs, 16 * u, db * 32, lane);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32x32x16(vfr, pf[rb], oacc[rb][db]);
+        }
+      }
+    }
     // step t+1 must be resident; later steps may still be in flight
     if (SPARSE ? jn >= 0 : t + 1 < ntiles) {
       wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(SPARSE ? 0 : min(ST - 2, ntiles - t - 2));
@@ -489,7 +432,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int query = q0w + 32 * rb + c32;
-      const float lt = sum_halves(wv.l[rb]);
+      const float lt = sum_halves(l[rb]);
       const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
       if (query < N) {
         const size_t r = split * rows + (size_t)bh * N + query;
@@ -499,37 +442,46 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 #pragma unroll
           for (int g = 0; g < 4; ++g)
             *reinterpret_cast<float4*>(Op + db * 32 + 8 * g + 4 * h) =
-                make_float4(wv.oacc[rb][db][4 * g] * inv, wv.oacc[rb][db][4 * g + 1] * inv,
-                            wv.oacc[rb][db][4 * g + 2] * inv, wv.oacc[rb][db][4 * g + 3] * inv);
-        if (h == 0) sa.Lpart[r] = lt > 0.f ? (wv.m[rb] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+                make_float4(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv,
+                            oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
+        if (h == 0) sa.Lpart[r] = lt > 0.f ? (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
       }
     }
     return;
   }
 
-  if constexpr (!C::QL) {
-    wv.store(O + hoff, LSE + (size_t)bh * N, DROP ? dr.scale : 1.f);
-  } else {
-    // Epilogue through LDS: O = acc / l (bf16), LSE = m ln2 + ln l (fp32,
-    // natural log).
+  // Epilogue: O = acc / l (bf16), LSE = m ln2 + ln l (fp32, natural log).
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int query = q0w + 32 * rb + c32;
-      const float lt = sum_halves(wv.l[rb]);  // >= 1: the row maximum has weight >= 1
-      const float inv = DROP ? __builtin_amdgcn_rcpf(lt) * dr.scale : __builtin_amdgcn_rcpf(lt);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int query = q0w + 32 * rb + c32;
+    const float lt = sum_halves(l[rb]);  // >= 1: the row maximum has weight >= 1
+    const float inv = DROP ? __builtin_amdgcn_rcpf(lt) * dr.scale : __builtin_amdgcn_rcpf(lt);
+    if constexpr (C::QL) {
       // O fragment (dims db*32 + 8g + 4h + 0..3 of this lane's row) into
       // this wavefront's rows of the Q staging tile
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const uint32_t lo = pack_bf16x2(wv.oacc[rb][db][4 * g] * inv, wv.oacc[rb][db][4 * g + 1] * inv);
-          const uint32_t hi = pack_bf16x2(wv.oacc[rb][db][4 * g + 2] * inv, wv.oacc[rb][db][4 * g + 3] * inv);
+          const uint32_t lo = pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv);
+          const uint32_t hi = pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
           *reinterpret_cast<uint2*>(qs + tile_off<D>(w * C::RW + 32 * rb + c32, db * 32 + 8 * g + 4 * h)) =
               make_uint2(lo, hi);
         }
-      if (h == 0 && query < N) LSE[(size_t)bh * N + query] = (wv.m[rb] + __builtin_amdgcn_logf(lt)) * kLn2;
+    } else if (query < N) {
+      bf16_t* Or = O + hoff + (size_t)query * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t lo = pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv);
+          const uint32_t hi = pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(Or + db * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
+        }
     }
+    if (h == 0 && query < N) LSE[(size_t)bh * N + query] = (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2;
+  }
+  if constexpr (C::QL) {
     // rows back out of LDS as whole 16-byte chunks: 8 lanes per row, so each
     // store instruction writes 8 complete rows
     constexpr int CPR = D / 8;
