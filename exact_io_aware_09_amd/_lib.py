@@ -52,6 +52,8 @@ SIGNATURES = {
     "fa_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_backward": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                          _I, _I, _I, _I, _F, _I, _I, _VP]),
+    "fa_backward_noalloc": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                 _I, _I, _I, _I, _F, _I, _I, _VP]),
     "fa_backward_preprocess": (_I, [_VP, _VP, _VP, _VP, _SZ, _I, _I, _I, _I, _I, _VP]),
     "fa_backward_dkdv": (_I, [_VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP,
                               _I, _I, _I, _I, _F, _I, _I, _VP]),
@@ -180,6 +182,13 @@ def fa_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, 
     return int(load().fa_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace,
                                   workspace_bytes, B, H, N, d, float(scale), int(causal),
                                   int(dtype), stream))
+
+
+def fa_backward_noalloc(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, scale, causal, dtype,
+                        stream) -> int:
+    """Raw call: device pointers as ints, returns the C return code."""
+    return int(load().fa_backward_noalloc(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d,
+                                          float(scale), int(causal), int(dtype), stream))
 
 
 def fa_backward_preprocess(O, dO, LSE, workspace, workspace_bytes, B, H, N, d, dtype,

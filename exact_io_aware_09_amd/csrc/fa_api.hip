@@ -5,10 +5,53 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "fa.h"
 #include "fa_launch.h"
 
+// Device scratch of fa_backward_noalloc: the backward workspace (-D and
+// LSE * log2(e)) for callers that cannot allocate.  Each GPU the library
+// runs on holds its own copy from module load until the process ends.  In
+// host code the name `scratch` is only a stand-in for the symbol: kernels
+// receive the device address that hipGetSymbolAddress returns for the
+// current device (scratch_address below), never the name itself.
+__device__ __attribute__((aligned(256))) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Per-device address of `scratch`, looked up once per device (with that
+// device current) and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Address of this device's scratch for work enqueued on `stream`: the
+// stream must belong to the current device (the symbol is looked up for the
+// current device).
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA_ERR_HIP;
+  if (dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return FA_ERR_HIP;
+    if ((int)sdev != dev) return FA_ERR_INVALID_ARG;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+        return FA_ERR_HIP;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return FA_OK;
+}
 
 constexpr int kVersion = 400;  // 0.4.0
 
@@ -274,6 +317,33 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
   const fa::Problem p{B, H, N, d, scale, causal != 0};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* Dws = static_cast<float*>(workspace);
+  hipError_t e =
+      (dtype == FA_BF16)
+          ? fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, fa::kStagesGrad, s)
+          : fa::launch_backward_f32((const float*)Q, (const float*)K, (const float*)V,
+                                    (const float*)O, (const float*)dO, LSE, (float*)dQ,
+                                    (float*)dK, (float*)dV, Dws, p, fa::kStagesGrad, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_backward_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                        const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
+                        float scale, int causal, int dtype, void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_backward_workspace_bytes(B, H, N, d, dtype);
+  if (need == 0 || need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_NO_WORKSPACE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
+    return FA_ERR_MISALIGNED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  rc = scratch_address(s, &ws);
+  if (rc != FA_OK) return rc;
+  // the same kernels as fa_backward, with the workspace in the scratch
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  float* Dws = static_cast<float*>(ws);
   hipError_t e =
       (dtype == FA_BF16)
           ? fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, p, fa::kStagesGrad, s)

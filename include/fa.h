@@ -270,6 +270,30 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O,
                 void* stream);
 
 /*
+ * fa_backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The two workspace vectors live in a
+ * device scratch array compiled into the library, FA_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) per GPU, held from module load until the process ends; problems
+ * whose fa_backward_workspace_bytes() exceeds it (more than about 2.09
+ * million query rows B*H*N) return FA_ERR_NO_WORKSPACE before anything is
+ * enqueued.  Nothing is allocated or freed: the call enqueues the same two
+ * kernels as fa_backward (identical results, bit for bit) on `stream`, which
+ * must belong to the current device (FA_ERR_INVALID_ARG otherwise).  The
+ * scratch address is looked up once per device on the first call.  Every
+ * call on a GPU shares that GPU's scratch and leaves its contents behind:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be serialised by the caller; a call needs no cleared scratch (the dQ
+ * kernel writes every value the dK/dV kernel reads).  Other arguments and
+ * errors as fa_backward.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_backward_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                        int B, int H, int N, int d, float scale, int causal, int dtype,
+                        void* stream);
+
+/*
  * The stages of fa_backward as separate calls, for callers that want to
  * schedule or time them individually.  Enqueuing fa_backward_dq and then
  * fa_backward_dkdv on one stream computes exactly what fa_backward computes

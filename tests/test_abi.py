@@ -231,3 +231,17 @@ def test_every_kernel_source_is_a_build_unit():
             assert "#define FA_D" in text and f'#include "{base}"' in text
         else:
             assert extra == []
+
+
+def test_backward_noalloc_validation():
+    # checked before anything touches a device: bad arguments, and problems
+    # whose workspace exceeds the library's 16 MiB scratch
+    f = _lib.load().fa_backward_noalloc
+    P = [64] * 9
+    assert f(*P, 64, 16, 4096, 64, 0.125, 1, _lib.FA_BF16, None) == _lib.FA_ERR_NO_WORKSPACE
+    assert f(*P[:8], None, 1, 1, 128, 64, 0.125, 0, _lib.FA_BF16, None) == _lib.FA_ERR_INVALID_ARG
+    assert f(*P, 1, 1, 128, 48, 0.125, 0, _lib.FA_BF16, None) == _lib.FA_ERR_UNSUPPORTED
+    assert f(*P, 1, 1, 128, 64, -1.0, 0, _lib.FA_BF16, None) == _lib.FA_ERR_INVALID_ARG
+    assert f(*([24] + P[1:]), 1, 1, 128, 64, 0.125, 0, _lib.FA_BF16, None) == _lib.FA_ERR_MISALIGNED
+    # the largest row count that fits: workspace of exactly 16 MiB or less
+    assert _lib.fa_backward_workspace_bytes(64, 16, 1024, 64, _lib.FA_BF16) <= 16 << 20
