@@ -47,9 +47,16 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2_medium")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward kernel")
-    ap.add_argument("--mask", choices=("none", "band"), default="none",
+    ap.add_argument("--mask", choices=("none", "band", "band_global"), default="none",
                     help="block-sparse attention through fa_forward_sparse / fa_backward_sparse "
-                         "with a 128x128 tile mask: 'band' = tiles within two of the diagonal")
+                         "with a 128x128 tile mask: 'band' = tiles within two of the diagonal, "
+                         "'band_global' = the band plus tile row 0 and tile column 0 (the first "
+                         "128 positions as global tokens)")
+    ap.add_argument("--balanced", action="store_true",
+                    help="with --mask: run fa_forward_sparse_balanced / "
+                         "fa_backward_sparse_balanced over a schedule built from the mask")
+    ap.add_argument("--seg", type=int, default=0,
+                    help="with --balanced: most tiles per work item (0 = the library's default)")
     ap.add_argument("--splits", type=int, default=1,
                     help="forward through fa_forward_split with this many key ranges "
                          "(implies --fwd-only when > 1)")
@@ -107,6 +114,19 @@ def band_mask(N):
     nb = (N + 127) // 128
     i = torch.arange(nb)
     return ((i.unsqueeze(1) - i.unsqueeze(0)).abs() <= 2).to(torch.int32)
+
+
+def tile_mask(kind, N):
+    """'band', or 'band_global': the band plus a global first tile row and column,
+    whose whole work falls on one workgroup per head unless it is split."""
+    m = band_mask(N)
+    if kind == "band_global":
+        m[0, :] = 1
+        m[:, 0] = 1
+    return m
+
+
+MASK_NAMES = {"band": "band |I-J|<=2", "band_global": "band |I-J|<=2 + global tile row/column 0"}
 
 
 def mask_pairs(w, mask) -> int:
@@ -372,9 +392,19 @@ def main(argv=None):
         k8, ks = fa.quantize_fp8(k)
         v8, vs = fa.quantize_fp8(v, keys=True)
         P8 = [t.data_ptr() for t in (q8, qs, k8, ks, v8, vs)]
+    if args.balanced and not sparse:
+        print("bench.py: --balanced needs --mask", file=sys.stderr)
+        return 2
     fused = sparse or drop  # one backward call: events around forward and backward only
-    maskd = band_mask(N).to(dev) if sparse else None
+    maskc = tile_mask(args.mask, N) if sparse else None
+    maskd = maskc.to(dev) if sparse else None
     wsb = fa.workspace_bytes(B, H, N, d, w.dtype)
+    sched = None
+    if args.balanced:
+        sched = fa.sparse_schedule(maskc, N, w.causal, B, H, seg_tiles=args.seg).to(dev)
+        sh, sdv = sched.host.ctypes.data, sched.device_copy.data_ptr()
+        wsb = max(wsb, _lib.fa_sparse_workspace_bytes(sh, B, H, N, d, 0),
+                  _lib.fa_sparse_workspace_bytes(sh, B, H, N, d, 1))
     if args.splits > 1:
         wsb = max(wsb, _lib.fa_forward_split_workspace_bytes(B, H, N, d, args.splits, dt))
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
@@ -390,6 +420,19 @@ def main(argv=None):
         """One step; if `ev` is given, record events between the kernels."""
         rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
         rec(0)
+        if sched is not None:
+            call(_lib.fa_forward_sparse_balanced(P[0], P[1], P[2], P[3], P[4], sh, sdv, P[9], wsb,
+                                                 B, H, N, d, w.scale, int(w.causal), dt, sp),
+                 "fa_forward_sparse_balanced")
+            rec(1)
+            if args.fwd_only:
+                return
+            call(_lib.fa_backward_sparse_balanced(P[0], P[1], P[2], P[3], P[5], P[4], sh, sdv,
+                                                  P[6], P[7], P[8], P[9], wsb, B, H, N, d,
+                                                  w.scale, int(w.causal), dt, sp),
+                 "fa_backward_sparse_balanced")
+            rec(2)
+            return
         if sparse:
             call(_lib.fa_forward_sparse(P[0], P[1], P[2], P[3], P[4], maskd.data_ptr(), B, H, N,
                                         d, w.scale, int(w.causal), dt, sp), "fa_forward_sparse")
@@ -462,7 +505,7 @@ def main(argv=None):
 
     fwd_fl, bwd_fl = credited_flops(w)
     if sparse:
-        fwd_fl = 4 * w.d * mask_pairs(w, band_mask(N))
+        fwd_fl = 4 * w.d * mask_pairs(w, maskc)
         bwd_fl = fwd_fl * 5 // 2
     total_fl = fwd_fl if args.fwd_only else fwd_fl + bwd_fl
     tflops = total_fl / (ms_step * 1e-3) / 1e12
@@ -471,7 +514,7 @@ def main(argv=None):
         # the forward's two contractions (fwd_sparse), or dQ's three plus dK/dV's four, per
         # visible pair of the mask
         per = 2 if dom == "fwd_sparse" else 7
-        bound, amount = "mfma", per * 2 * w.d * mask_pairs(w, band_mask(N))
+        bound, amount = "mfma", per * 2 * w.d * mask_pairs(w, maskc)
     elif args.fp8:
         # the forward's two contractions per visible pair, at the fp8 peak
         bound, amount = "mfma", 4 * w.d * visible_pairs(w)
@@ -492,7 +535,8 @@ def main(argv=None):
         "metric": METRIC if (args.workload == "gpt2_medium" and not args.fwd_only and not drop)
         else (f"attention {'fwd' if args.fwd_only else 'fwd+bwd'} TFLOP/s ({args.workload}"
               + (f", {args.splits} key ranges)" if args.splits > 1 else
-                 ", block-sparse band tiles, FLOPs of visible pairs)" if sparse else
+                 f", block-sparse {args.mask} tiles{', balanced' if args.balanced else ''}, "
+                 "FLOPs of visible pairs)" if sparse else
                  f", dropout {args.dropout})" if drop else
                  ", FP8 E4M3 with block scales)" if args.fp8 else ")")),
         "value": round(tflops, 2),
@@ -509,8 +553,14 @@ def main(argv=None):
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                    "scale": w.scale, "input_dtype": dtype_name,
                    "step": "forward" if args.fwd_only else "forward+backward",
-                   **({"tile_mask": "band |I-J|<=2", "visible_pairs": mask_pairs(w, band_mask(N))}
+                   **({"tile_mask": MASK_NAMES[args.mask], "visible_pairs": mask_pairs(w, maskc)}
                       if sparse else {}),
+                   **({"schedule": {"seg": sched.field("SEG"),
+                                    "split_rows": sched.field("N_LONG_ROWS"),
+                                    "split_cols": sched.field("N_LONG_COLS"),
+                                    "row_items": sched.field("N_ROWS"),
+                                    "col_items": sched.field("N_COLS")}}
+                      if sched is not None else {}),
                    **({"splits": args.splits} if args.splits > 1 else {}),
                    **({"dropout": args.dropout, "seed": DROPOUT_SEED} if drop else {}),
                    **({"fp8": "E4M3, power-of-two scale per 32 elements"} if args.fp8 else {})},

@@ -26,6 +26,16 @@ FA_ERR_MISALIGNED = -3
 FA_ERR_NO_WORKSPACE = -4
 FA_ERR_HIP = -5
 
+# Header fields of a balanced block-sparse schedule (int32 indices; fa.h FA_SCHED_*)
+FA_SCHED_FIELDS = {
+    "MAGIC": 0, "HEADER_INTS": 1, "NB": 2, "CAUSAL": 3, "SEG": 4, "N_ROWS": 5, "N_COLS": 6,
+    "ROW_SLOTS": 7, "COL_SLOTS": 8, "N_LONG_ROWS": 9, "N_LONG_COLS": 10, "OFF_ROWS": 11,
+    "OFF_COLS": 12, "OFF_LONG_ROWS": 13, "OFF_LONG_COLS": 14, "OFF_LISTS": 15, "LIST_LEN": 16,
+    "TOTAL": 17, "NNZ": 18,
+}
+FA_SCHED_HEADER = 20
+FA_SCHED_MAGIC_VALUE = 0x46534221
+
 # name -> (restype, argtypes); the single source for the exported symbol list
 _VP = ctypes.c_void_p
 _I = ctypes.c_int
@@ -42,6 +52,12 @@ SIGNATURES = {
     "fa_forward_sparse": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _F, _I, _I, _VP]),
     "fa_backward_sparse": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                                 _I, _I, _I, _I, _F, _I, _I, _VP]),
+    "fa_sparse_schedule": (_I, [_VP, _I, _I, _I, _I, _I, _VP, _SZ, _VP]),
+    "fa_sparse_workspace_bytes": (_SZ, [_VP, _I, _I, _I, _I, _I]),
+    "fa_forward_sparse_balanced": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
+                                        _I, _I, _I, _I, _F, _I, _I, _VP]),
+    "fa_backward_sparse_balanced": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                         _VP, _SZ, _I, _I, _I, _I, _F, _I, _I, _VP]),
     "fa_forward_dropout": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _F, _I, _F, _U64, _I, _VP]),
     "fa_backward_dropout": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                                  _I, _I, _I, _I, _F, _I, _F, _U64, _I, _VP]),
@@ -136,6 +152,32 @@ def fa_backward_sparse(Q, K, V, O, dO, LSE, block_mask, dQ, dK, dV, workspace, w
     return int(load().fa_backward_sparse(Q, K, V, O, dO, LSE, block_mask, dQ, dK, dV, workspace,
                                          workspace_bytes, B, H, N, d, float(scale), int(causal),
                                          int(dtype), stream))
+
+
+def fa_sparse_schedule(block_mask, N, causal, B, H, seg_tiles, schedule, schedule_ints,
+                       needed_ints) -> int:
+    """block_mask, schedule: host addresses; needed_ints: address of a size_t."""
+    return int(load().fa_sparse_schedule(block_mask, N, causal, B, H, seg_tiles, schedule,
+                                         schedule_ints, needed_ints))
+
+
+def fa_sparse_workspace_bytes(schedule, B, H, N, d, backward) -> int:
+    return int(load().fa_sparse_workspace_bytes(schedule, B, H, N, d, backward))
+
+
+def fa_forward_sparse_balanced(Q, K, V, O, LSE, schedule, schedule_dev, workspace,
+                               workspace_bytes, B, H, N, d, scale, causal, dtype, stream) -> int:
+    return int(load().fa_forward_sparse_balanced(Q, K, V, O, LSE, schedule, schedule_dev,
+                                                 workspace, workspace_bytes, B, H, N, d,
+                                                 float(scale), causal, dtype, stream))
+
+
+def fa_backward_sparse_balanced(Q, K, V, O, dO, LSE, schedule, schedule_dev, dQ, dK, dV,
+                                workspace, workspace_bytes, B, H, N, d, scale, causal, dtype,
+                                stream) -> int:
+    return int(load().fa_backward_sparse_balanced(Q, K, V, O, dO, LSE, schedule, schedule_dev,
+                                                  dQ, dK, dV, workspace, workspace_bytes, B, H,
+                                                  N, d, float(scale), causal, dtype, stream))
 
 
 def fa_forward_dropout(Q, K, V, O, LSE, B, H, N, d, scale, causal, p_drop, seed, dtype,

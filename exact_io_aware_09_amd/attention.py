@@ -6,6 +6,9 @@ outputs with ``torch.empty`` on the inputs' device and call ``fa_forward`` /
 """
 from __future__ import annotations
 
+import ctypes
+
+import numpy as np
 import torch
 
 from . import _lib
@@ -149,6 +152,112 @@ def backward_sparse(q, k, v, o, do, lse, block_mask, scale: float, causal: bool 
                                  _stream(q.device))
     if rc != _lib.FA_OK:
         raise _lib.FAError(rc, "fa_backward_sparse")
+    return dq, dk, dv
+
+
+class SparseSchedule:
+    """A balanced block-sparse schedule: the int32 array ``fa_sparse_schedule``
+    wrote (``host``) and, once ``to(device)`` has run, its device copy."""
+
+    def __init__(self, host: np.ndarray):
+        self.host = host
+        self.device_copy = None
+
+    def field(self, name: str) -> int:
+        return int(self.host[_lib.FA_SCHED_FIELDS[name]])
+
+    def to(self, device):
+        self.device_copy = torch.from_numpy(self.host).to(device)
+        return self
+
+    def _section(self, off, count, width=4):
+        o = self.field(off)
+        return self.host[o:o + width * count].reshape(count, width) if width > 1 else \
+            self.host[o:o + count]
+
+    def rows(self):
+        """Row items [n, 4]: tile, list offset, tile count, slot word."""
+        return self._section("OFF_ROWS", self.field("N_ROWS"))
+
+    def cols(self):
+        return self._section("OFF_COLS", self.field("N_COLS"))
+
+    def long_rows(self):
+        return self._section("OFF_LONG_ROWS", self.field("N_LONG_ROWS"))
+
+    def long_cols(self):
+        return self._section("OFF_LONG_COLS", self.field("N_LONG_COLS"))
+
+    def lists(self):
+        return self._section("OFF_LISTS", self.field("LIST_LEN"), width=1)
+
+
+def sparse_schedule(block_mask, N: int, causal: bool, B: int, H: int, seg_tiles: int = 0):
+    """Builds the balanced schedule of a tile mask (host int32 [nb, nb], numpy or CPU tensor)."""
+    if isinstance(block_mask, torch.Tensor):
+        block_mask = block_mask.detach().cpu().numpy()
+    m = np.ascontiguousarray(block_mask, dtype=np.int32)
+    nb = (N + 127) // 128
+    if m.shape != (nb, nb):
+        raise ValueError(f"block_mask must be [{nb}, {nb}]")
+    needed = ctypes.c_size_t(0)
+    rc = _lib.fa_sparse_schedule(m.ctypes.data, N, int(bool(causal)), B, H, seg_tiles, None, 0,
+                                 ctypes.addressof(needed))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_sparse_schedule")
+    host = np.zeros(needed.value, dtype=np.int32)
+    rc = _lib.fa_sparse_schedule(m.ctypes.data, N, int(bool(causal)), B, H, seg_tiles,
+                                 host.ctypes.data, host.size, ctypes.addressof(needed))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_sparse_schedule")
+    return SparseSchedule(host)
+
+
+def _sched_check(sched, q):
+    if not isinstance(sched, SparseSchedule) or sched.device_copy is None \
+            or sched.device_copy.device != q.device:
+        raise ValueError("schedule must be a SparseSchedule copied to the inputs' device")
+
+
+def forward_sparse_balanced(q, k, v, sched, scale: float, causal: bool = False):
+    """Block-sparse forward over a balanced schedule: (O, LSE)."""
+    _check("q", q)
+    _check("k", k, q)
+    _check("v", v, q)
+    B, H, N, d, dt = _dims(q)
+    _sched_check(sched, q)
+    need = _lib.fa_sparse_workspace_bytes(sched.host.ctypes.data, B, H, N, d, 0)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    rc = _lib.fa_forward_sparse_balanced(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                         lse.data_ptr(), sched.host.ctypes.data,
+                                         sched.device_copy.data_ptr(), ws.data_ptr(), ws.numel(),
+                                         B, H, N, d, scale, int(bool(causal)), dt,
+                                         _stream(q.device))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_forward_sparse_balanced")
+    return o, lse
+
+
+def backward_sparse_balanced(q, k, v, o, do, lse, sched, scale: float, causal: bool = False):
+    """Block-sparse backward over a balanced schedule: (dQ, dK, dV)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, None if name == "q" else q)
+    B, H, N, d, dt = _dims(q)
+    _sched_check(sched, q)
+    _check_lse(lse, q)
+    need = _lib.fa_sparse_workspace_bytes(sched.host.ctypes.data, B, H, N, d, 1)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    rc = _lib.fa_backward_sparse_balanced(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                          do.data_ptr(), lse.data_ptr(), sched.host.ctypes.data,
+                                          sched.device_copy.data_ptr(), dq.data_ptr(),
+                                          dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+                                          B, H, N, d, scale, int(bool(causal)), dt,
+                                          _stream(q.device))
+    if rc != _lib.FA_OK:
+        raise _lib.FAError(rc, "fa_backward_sparse_balanced")
     return dq, dk, dv
 
 

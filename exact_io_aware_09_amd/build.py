@@ -38,6 +38,7 @@ UNITS = [
     ("fa_fp8.hip", []),
     ("fa_fp8_d256.hip", VGPR_FORM),
     ("fa_f32.hip", []),
+    ("fa_sched.hip", []),
 ]
 SOURCES = [u for u, _ in UNITS]
 

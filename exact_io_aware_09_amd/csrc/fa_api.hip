@@ -98,6 +98,27 @@ size_t split_lse_offset(size_t rows, int d, int splits) {
   return ((size_t)splits * rows * d * sizeof(float) + 255) & ~(size_t)255;
 }
 
+// Balanced schedule: launch sizes from the host copy, item pointers into the
+// device copy, partial buffers carved out of the workspace.
+int sched_args(const int* schedule, const int* schedule_dev, int N, int causal,
+                      fa::SchedView& v, fa::SparseArgs& sp) {
+  if (!fa::read_schedule(schedule, v) || schedule_dev == nullptr) return FA_ERR_INVALID_ARG;
+  if (v.nb != (N + 127) / 128 || v.causal != causal) return FA_ERR_INVALID_ARG;
+  if (!aligned16(schedule_dev)) return FA_ERR_MISALIGNED;
+  sp.nb = v.nb;
+  sp.rows = schedule_dev + v.off_rows;
+  sp.cols = schedule_dev + v.off_cols;
+  sp.n_rows = v.n_rows;
+  sp.n_cols = v.n_cols;
+  sp.lists = schedule_dev + v.off_lists;
+  sp.list_len = v.list_len;
+  sp.row_slots = v.row_slots;
+  sp.col_slots = v.col_slots;
+  return FA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
 
 extern "C" {
@@ -213,6 +234,82 @@ int fa_backward_sparse(const void* Q, const void* K, const void* V, const void* 
   hipError_t e = fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV,
                                           static_cast<float*>(workspace), p, fa::kStagesGrad,
                                           reinterpret_cast<hipStream_t>(stream), sp);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_forward_sparse_balanced(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               const int* schedule, const int* schedule_dev, void* workspace,
+                               size_t workspace_bytes, int B, int H, int N, int d, float scale,
+                               int causal, int dtype, void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !O || !LSE || !schedule) return FA_ERR_INVALID_ARG;
+  fa::SchedView v;
+  fa::SparseArgs sp;
+  rc = sched_args(schedule, schedule_dev, N, causal, v, sp);
+  if (rc != FA_OK) return rc;
+  const size_t need = fa_sparse_workspace_bytes(schedule, B, H, N, d, 0);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_NO_WORKSPACE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE) ||
+      (need > 0 && !aligned16(workspace)))
+    return FA_ERR_MISALIGNED;
+  const size_t tile = (size_t)B * H * 128;
+  char* ws = static_cast<char*>(workspace);
+  if (need > 0) {
+    sp.part_o = reinterpret_cast<float*>(ws);
+    sp.part_l = reinterpret_cast<float*>(ws + align256((size_t)v.row_slots * tile * d * 4));
+  }
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = fa::launch_forward_bf16(Q, K, V, O, LSE, p, s, sp);
+  if (e == hipSuccess)
+    e = fa::launch_merge_rows(sp.part_o, sp.part_l, v.row_slots, schedule_dev + v.off_long_rows,
+                              v.n_long_rows, O, LSE, p, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_backward_sparse_balanced(const void* Q, const void* K, const void* V, const void* O,
+                                const void* dO, const float* LSE, const int* schedule,
+                                const int* schedule_dev, void* dQ, void* dK, void* dV,
+                                void* workspace, size_t workspace_bytes, int B, int H, int N,
+                                int d, float scale, int causal, int dtype, void* stream) {
+  int rc = check_common(B, H, N, d, scale, causal, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !schedule)
+    return FA_ERR_INVALID_ARG;
+  fa::SchedView v;
+  fa::SparseArgs sp;
+  rc = sched_args(schedule, schedule_dev, N, causal, v, sp);
+  if (rc != FA_OK) return rc;
+  const size_t need = fa_sparse_workspace_bytes(schedule, B, H, N, d, 1);
+  if (need == 0 || !workspace || workspace_bytes < need) return FA_ERR_NO_WORKSPACE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) ||
+      !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
+  const size_t tile = (size_t)B * H * 128;
+  char* ws = static_cast<char*>(workspace);
+  size_t at = align256(fa_backward_workspace_bytes(B, H, N, d, dtype));
+  sp.part_dq = reinterpret_cast<float*>(ws + at);
+  at += align256((size_t)v.row_slots * tile * d * 4);
+  sp.part_dk = reinterpret_cast<float*>(ws + at);
+  at += align256((size_t)v.col_slots * tile * d * 4);
+  sp.part_dv = reinterpret_cast<float*>(ws + at);
+  const fa::Problem p{B, H, N, d, scale, causal != 0};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = fa::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV,
+                                          reinterpret_cast<float*>(ws), p, fa::kStagesGrad, s, sp);
+  if (e == hipSuccess)
+    e = fa::launch_sum_parts(sp.part_dq, v.row_slots, schedule_dev + v.off_long_rows,
+                             v.n_long_rows, dQ, p, s);
+  if (e == hipSuccess)
+    e = fa::launch_sum_parts(sp.part_dk, v.col_slots, schedule_dev + v.off_long_cols,
+                             v.n_long_cols, dK, p, s);
+  if (e == hipSuccess)
+    e = fa::launch_sum_parts(sp.part_dv, v.col_slots, schedule_dev + v.off_long_cols,
+                             v.n_long_cols, dV, p, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -158,6 +158,13 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   const int h = lane >> 5, c32 = lane & 31;
   int bh, kb;  // causal: low key blocks see the most queries, run them first
   grouped_order(xcd_remap(blockIdx.x, BH * nkb), nkb, BH, G, bh, kb);
+  // balanced schedule: item kb names the tile column and its run of tiles
+  int list_off = 0, list_cnt = -1, slotw = -1;
+  if constexpr (SPARSE) {
+    if (sp.cols != nullptr &&
+        !sched_item(sp.cols, kb, sp.nb, sp.list_len, sp.col_slots, kb, list_off, list_cnt, slotw))
+      return;
+  }
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rq = make_copy_rsrc(Q + hoff, head_bytes);
@@ -182,7 +189,10 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
   const int qstart = CAUSAL ? (k0 / C::BQ) * C::BQ : 0;
   const int nchunks = (N - qstart + C::BQ - 1) / C::BQ;
   // query chunks visited: dense from qstart, or those of the set tiles
-  const BlockWalk<C::BQ, SPARSE> walk{N, (const_int_ptr)(sp.mask + kb), sp.nb, sp.nb - 1};
+  BlockWalk<C::BQ, SPARSE> walk{N,
+                                list_cnt >= 0 ? (const_int_ptr)sp.lists + list_off
+                                              : (const_int_ptr)(sp.mask + kb),
+                                sp.nb, sp.nb - 1, list_cnt};
   const int ifirst = SPARSE ? walk.first(qstart) : qstart;
 
   auto fetch_at = [&](int i0, auto S) {
@@ -433,6 +443,35 @@ void bwd_dkdv_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict
 #pragma unroll
         for (int r = 0; r < 16; ++r) dvacc[kk][db][r] *= dr.scale;
   }
+  if constexpr (SPARSE) {
+    if (slotw >= 0) {
+      // segment of a split tile column: its shares of dK and dV (float32)
+      const size_t prow = ((size_t)(slotw >> 1) * BH + bh) * C::BK;
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int key = k0w + 32 * kk + c32;
+        if (key < N) {
+          float* Pk = sp.part_dk + (prow + (key - k0)) * D;
+          float* Pv = sp.part_dv + (prow + (key - k0)) * D;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int col = db * 32 + 8 * g + 4 * h;
+              if constexpr (DKP)
+                *reinterpret_cast<float4*>(Pk + col) =
+                    make_float4(dkacc[kk][db][4 * g] * scale, dkacc[kk][db][4 * g + 1] * scale,
+                                dkacc[kk][db][4 * g + 2] * scale, dkacc[kk][db][4 * g + 3] * scale);
+              if constexpr (DVP)
+                *reinterpret_cast<float4*>(Pv + col) =
+                    make_float4(dvacc[kk][db][4 * g], dvacc[kk][db][4 * g + 1],
+                                dvacc[kk][db][4 * g + 2], dvacc[kk][db][4 * g + 3]);
+            }
+        }
+      }
+      return;
+    }
+  }
   if constexpr (C::KL) {
     // fragments (dims db*32 + 8g + 4h + 0..3 of this lane's key rows) into
     // this wavefront's rows of the staging tiles, then out as whole rows:
@@ -563,7 +602,14 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
   const int h = lane >> 5, c32 = lane & 31;
   int bh, rank;
   grouped_order(xcd_remap(blockIdx.x, BH * nqb), nqb, BH, G, bh, rank);
-  const int qb = CAUSAL ? (nqb - 1 - rank) : rank;  // longest causal blocks first
+  int qb = CAUSAL ? (nqb - 1 - rank) : rank;  // longest causal blocks first
+  // balanced schedule: item `rank` names the tile row and its run of tiles
+  int list_off = 0, list_cnt = -1, slotw = -1;
+  if constexpr (SPARSE) {
+    if (sp.rows != nullptr &&
+        !sched_item(sp.rows, rank, sp.nb, sp.list_len, sp.row_slots, qb, list_off, list_cnt, slotw))
+      return;
+  }
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rk = make_copy_rsrc(K + hoff, head_bytes);
@@ -583,7 +629,10 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
   const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
   // keys visited: dense from 0, or the blocks of the set tiles
-  const BlockWalk<BC, SPARSE> walk{kend, (const_int_ptr)(sp.mask + (size_t)qb * sp.nb), 1, CAUSAL ? qb : sp.nb - 1};
+  BlockWalk<BC, SPARSE> walk{kend,
+                             list_cnt >= 0 ? (const_int_ptr)sp.lists + list_off
+                                           : (const_int_ptr)(sp.mask + (size_t)qb * sp.nb),
+                             1, CAUSAL ? qb : sp.nb - 1, list_cnt};
   const int jfirst = SPARSE ? walk.first(0) : 0;
 
   auto fetch_at = [&](int j0, auto S) {
@@ -650,7 +699,8 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = fmaf((float)of[rb][s][e], (float)ov[rb][s][e], part);
     dd[rb] = sum_halves(part);
-    if (h == 0 && query < N) {
+    // (of a split tile row, the first segment stores the row vectors)
+    if (h == 0 && query < N && (slotw < 0 || (slotw & 1))) {
       Dws[(size_t)bh * N + query] = -dd[rb];
       Lws[(size_t)bh * N + query] = lse2[rb];
     }
@@ -794,6 +844,28 @@ void bwd_dq_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__
     }
   }
 
+  if constexpr (SPARSE) {
+    if (slotw >= 0) {
+      // segment of a split tile row: its share of dQ (float32) for the sum
+      const size_t prow = ((size_t)(slotw >> 1) * BH + bh) * C::BR;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int query = q0w + 32 * rb + c32;
+        if (query < N) {
+          float* Pr = sp.part_dq + (prow + (query - q0)) * D;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<float4*>(Pr + db * 32 + 8 * g + 4 * h) =
+                  make_float4(dqacc[rb][db][4 * g] * scale, dqacc[rb][db][4 * g + 1] * scale,
+                              dqacc[rb][db][4 * g + 2] * scale, dqacc[rb][db][4 * g + 3] * scale);
+        }
+      }
+      return;
+    }
+  }
+
   if constexpr (C::QL) {
     // fragments (dims db*32 + 8g + 4h + 0..3 of this lane's row) into this
     // wavefront's rows of the Q staging tile, then out as whole rows: 8 lanes
@@ -864,7 +936,8 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
   }
   if (stages & kStageDq) {
     using C = DqCfg<D, NWQ, RBQ, BC, STQ>;
-    const int nqb = (p.N + C::BR - 1) / C::BR;
+    // workgroups per head: query blocks, or the balanced schedule's row items
+    const int nqb = SPARSE && sp.rows != nullptr ? sp.n_rows : (p.N + C::BR - 1) / C::BR;
     const long long grid = (long long)BH * nqb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int G = head_group(OCCQ * 4 / NWQ, nqb);
@@ -877,7 +950,8 @@ hipError_t run_bwd(const void* Q, const void* K, const void* V, const void* O, c
   }
   if (stages & kStageDkDv) {
     using C = DkdvCfg<D, NWK, KBK, QB, STK>;
-    const int nkb = (p.N + C::BK - 1) / C::BK;
+    // workgroups per head: key blocks, or the balanced schedule's column items
+    const int nkb = SPARSE && sp.cols != nullptr ? sp.n_cols : (p.N + C::BK - 1) / C::BK;
     const long long grid = (long long)BH * nkb;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int G = head_group(OCCK * 4 / NWK, nkb);
@@ -926,11 +1000,11 @@ hipError_t run_bwd_cz(const void* Q, const void* K, const void* V, const void* O
                       const float* LSE, void* dQ, void* dK, void* dV, float* ws, const Problem& p,
                       unsigned stages, SparseArgs sp, hipStream_t stream, const DropArgs* dr) {
   if (dr != nullptr) {
-    if (sp.mask != nullptr) return hipErrorNotSupported;
+    if (sp.on()) return hipErrorNotSupported;
     return run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, CAUSAL, false, true>(
         Q, K, V, O, dO, LSE, dQ, dK, dV, ws, p, stages, sp, stream, *dr);
   }
-  if (sp.mask != nullptr) {
+  if (sp.on()) {
     // the sparse walk takes 128-key and 128-row blocks in two stages
     if constexpr (NWK * KBK * 32 == 128 && STK == 2 && NWQ * RBQ * 32 == 128 && STQ == 2)
       return run_bwd<D, NWK, KBK, QB, STK, OCCK, NWQ, RBQ, BC, STQ, OCCQ, CAUSAL, true>(

@@ -125,11 +125,14 @@ __device__ __forceinline__ void grouped_order(int L, int nblk, int BH, int G, in
 
 // Offsets of the blocks (BSZ rows or keys each, BSZ dividing 128) that a
 // workgroup visits in its main loop.  Dense: every block from `start` below
-// `end`.  Block-sparse: only the blocks inside the set 128 x 128 tiles of
-// the workgroup's row (or column) of the tile mask: tiles u <= hi, entry
-// m[u * stride] (int32; the index is uniform, so the entries are read
-// through the scalar cache).  Offsets are returned in increasing order, -1
-// after the last.
+// `end`.  Block-sparse, mask form (n < 0): only the blocks inside the set
+// 128 x 128 tiles of the workgroup's row (or column) of the tile mask:
+// tiles u <= hi, entry m[u * stride] (int32; the index is uniform, so the
+// entries are read through the scalar cache).  Block-sparse, list form
+// (n >= 0): the blocks of the n tiles whose indices m[0..n) lists in
+// increasing order (a balanced schedule's run of tiles); an index outside
+// [0, end / 128] ends the walk.  Offsets are returned in increasing order,
+// -1 after the last; next() must be given the offset returned last.
 // The mask is read-only for the whole launch: entries are loaded through
 // the constant address space, i.e. with scalar loads, which are waited on
 // with lgkmcnt and so never wait for the vector-memory copies in flight.
@@ -141,26 +144,55 @@ struct BlockWalk {
   int end;
   const_int_ptr m;
   int stride, hi;
+  int n = -1;  // list form: number of listed tiles
+  int p = 0;   // list form: position of the current tile
   // first set tile at or after tile u, as an offset, or -1
   __device__ __forceinline__ int tile_from(int u) const {
     while (u <= hi && m[u * stride] == 0) ++u;
     return (u <= hi && u * 128 < end) ? u * 128 : -1;
   }
-  // `start` is a multiple of 128 when SPARSE
-  __device__ __forceinline__ int first(int start) const {
-    if constexpr (SPARSE) return tile_from(start >> 7);
-    else return start < end ? start : -1;
+  // tile at list position q, as an offset, or -1
+  __device__ __forceinline__ int listed(int q) const {
+    if (q >= n) return -1;
+    const int u = m[q];
+    return (u >= 0 && u < (end + 127) / 128) ? u * 128 : -1;
   }
-  __device__ __forceinline__ int next(int off) const {
+  // `start` is a multiple of 128 when SPARSE (unused in the list form)
+  __device__ __forceinline__ int first(int start) {
+    if constexpr (SPARSE) {
+      if (n >= 0) {
+        p = 0;
+        return listed(0);
+      }
+      return tile_from(start >> 7);
+    } else {
+      return start < end ? start : -1;
+    }
+  }
+  __device__ __forceinline__ int next(int off) {
     const int o = off + BSZ;
     if constexpr (SPARSE) {
       if ((o & 127) != 0 && o < end) return o;
+      if (n >= 0) return listed(++p);
       return tile_from((off >> 7) + 1);
     } else {
       return o < end ? o : -1;
     }
   }
 };
+
+// Reads item `k` of a balanced schedule (4 ints, see SparseArgs) and checks
+// it against the schedule's sizes; false for an item that would leave them.
+__device__ __forceinline__ bool sched_item(const int* items, int k, int nb, int list_len,
+                                           int slots, int& t, int& off, int& cnt, int& slotw) {
+  const const_int_ptr it = (const_int_ptr)items + 4 * k;
+  t = it[0];
+  off = it[1];
+  cnt = it[2];
+  slotw = it[3];
+  return t >= 0 && t < nb && off >= 0 && cnt >= 0 && off <= list_len - cnt &&
+         (slotw == -1 || (slotw >= 0 && (slotw >> 1) < slots));
+}
 
 // 16-byte global load returning zeros when `ok` is false.
 __device__ __forceinline__ uint4 load16_or_zero(const bf16_t* p, bool ok) {

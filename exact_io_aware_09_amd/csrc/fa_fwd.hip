@@ -125,7 +125,14 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   } else {
     grouped_order(xcd_remap(blockIdx.x, BH * nqb), nqb, BH, G, bh, rank);
   }
-  const int qb = CAUSAL ? (nqb - 1 - rank) : rank;  // longest causal blocks first
+  int qb = CAUSAL ? (nqb - 1 - rank) : rank;  // longest causal blocks first
+  // balanced schedule: item `rank` names the tile row and its run of tiles
+  int list_off = 0, list_cnt = -1, slotw = -1;
+  if constexpr (SPARSE) {
+    if (sp.rows != nullptr &&
+        !sched_item(sp.rows, rank, sp.nb, sp.list_len, sp.row_slots, qb, list_off, list_cnt, slotw))
+      return;
+  }
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rk = make_copy_rsrc(K + hoff, head_bytes);
@@ -160,7 +167,10 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   }
 
   // keys visited: dense blocks kbase + t*BC, or the blocks of the set tiles
-  const BlockWalk<BC, SPARSE> walk{kend, (const_int_ptr)(sp.mask + (size_t)qb * sp.nb), 1, CAUSAL ? qb : sp.nb - 1};
+  BlockWalk<BC, SPARSE> walk{kend,
+                             list_cnt >= 0 ? (const_int_ptr)sp.lists + list_off
+                                           : (const_int_ptr)(sp.mask + (size_t)qb * sp.nb),
+                             1, CAUSAL ? qb : sp.nb - 1, list_cnt};
   const int jfirst = SPARSE ? walk.first(0) : kbase;
   if constexpr (SPARSE) {
     if (jfirst < 0) {
@@ -424,6 +434,33 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     }
   }
 
+  if constexpr (SPARSE) {
+    if (slotw >= 0) {
+      // segment of a split tile row: O normalised over the segment (float32)
+      // and the segment's log-sum-exp, for the merge kernel; every row sees
+      // the first key of the segment's first tile, so l > 0
+      const size_t prow = ((size_t)(slotw >> 1) * BH + bh) * C::BR;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int query = q0w + 32 * rb + c32;
+        const float lt = sum_halves(l[rb]);
+        const float inv = __builtin_amdgcn_rcpf(lt);
+        if (query < N) {
+          float* Op = sp.part_o + (prow + (query - q0)) * D;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<float4*>(Op + db * 32 + 8 * g + 4 * h) =
+                  make_float4(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv,
+                              oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
+          if (h == 0) sp.part_l[prow + (query - q0)] = (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2;
+        }
+      }
+      return;
+    }
+  }
+
   if constexpr (SPLIT) {
     // Partial result of the range: O normalised over it (float32, each lane
     // its 4-value groups db*32 + 8g + 4h + 0..3) and its log-sum-exp; a row
@@ -500,12 +537,13 @@ hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* 
                    const Problem& p, hipStream_t stream, SparseArgs sp) {
   using C = FwdCfg<D, NW, RB, BC, ST>;
   const int BH = p.B * p.H;
-  const int nqb = (p.N + C::BR - 1) / C::BR;
+  // workgroups per head: query blocks, or the balanced schedule's row items
+  const int nqb = sp.rows != nullptr ? sp.n_rows : (p.N + C::BR - 1) / C::BR;
   const long long grid = (long long)BH * nqb;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = p.scale * kLog2e;
   const int G = head_group(OCC * 4 / NW, nqb);
-  if (sp.mask != nullptr) {
+  if (sp.on()) {
     // the sparse walk takes 128-row query blocks in two stages
     if constexpr (C::BR == 128 && ST == 2)
       hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, true>), dim3((unsigned)grid),

@@ -26,10 +26,51 @@ struct SplitArgs {
 
 // Block-sparse attention: int32 tile mask [nb, nb] over 128 x 128 tiles of
 // (query rows, keys), shared by every head; nonzero = the tile is computed.
+//
+// Balanced schedule (rows != nullptr; the mask is then not read): the
+// forward and dQ kernels take work item `rank` of `rows`, the dK/dV kernel
+// item `rank` of `cols`, instead of tile row / column `rank`.  An item is 4
+// ints: tile index t, offset and count of its run of tile indices in
+// `lists` (increasing; the tiles of row t, or the query tiles of column t,
+// that the item visits), and the slot word: -1 when the item is the whole
+// row (column) and writes the final result, else 2 * slot + (1 for the
+// first segment of its row), and the item writes float32 partial results
+// to that slot of the part_* buffers ([slot][B*H][128][d], LSE parts
+// [slot][B*H][128]) for the merge kernels.
 struct SparseArgs {
   const int* mask = nullptr;
   int nb = 0;
+  const int* rows = nullptr;
+  const int* cols = nullptr;
+  int n_rows = 0, n_cols = 0;  // items in rows, cols
+  const int* lists = nullptr;
+  int list_len = 0;
+  int row_slots = 0, col_slots = 0;
+  float* part_o = nullptr;   // forward: O of a segment, normalised over it
+  float* part_l = nullptr;   // forward: the segment's log-sum-exp
+  float* part_dq = nullptr;  // dQ of a segment (scale applied)
+  float* part_dk = nullptr;  // dK of a segment (scale applied)
+  float* part_dv = nullptr;  // dV of a segment
+  bool on() const { return mask != nullptr || rows != nullptr; }
 };
+
+// Header of a balanced schedule (host copy), read and checked for internal
+// consistency by read_schedule.
+struct SchedView {
+  int nb, causal, n_rows, n_cols, row_slots, col_slots, n_long_rows, n_long_cols;
+  int off_rows, off_cols, off_long_rows, off_long_cols, off_lists, list_len, total;
+};
+bool read_schedule(const int* schedule, SchedView& v);
+
+// Rows of the merge kernels: for entry e of `longs` (4 ints: tile t, first
+// slot, number of slots, unused) and head bh, rows t*128 .. t*128+127 (< N).
+hipError_t launch_merge_rows(const float* part_o, const float* part_l, int slots, const int* longs,
+                             int n_longs, void* O, float* LSE, const Problem& p,
+                             hipStream_t stream);
+// Sum of the float32 partial gradients of every entry of `longs`, in slot
+// order, into the bf16 gradient rows.
+hipError_t launch_sum_parts(const float* part, int slots, const int* longs, int n_longs, void* out,
+                            const Problem& p, hipStream_t stream);
 
 // Dropout on the attention weights: 64-bit generator key (k0 low word), keep
 // threshold t in 1..256 on the 8-bit draws, kept weights scaled by 256 / t.

@@ -151,6 +151,84 @@ int fa_backward_sparse(const void* Q, const void* K, const void* V, const void* 
                        float scale, int causal, int dtype, void* stream);
 
 /*
+ * Balanced block-sparse attention.  fa_forward_sparse / fa_backward_sparse
+ * run one workgroup per tile row (forward, dQ) and per tile column (dK, dV),
+ * so a mask whose rows or columns differ much in length -- a sliding window
+ * with global tokens -- leaves a long row's whole work on one workgroup.
+ * The calls below take a schedule, built once per mask on the host, that
+ * cuts every row and column longer than `seg` set tiles into segments of at
+ * most `seg` tiles, one workgroup each, longest first; the segments of a
+ * split row write float32 partial results that small kernels then combine
+ * in a fixed order (forward: the merge of partial softmax results, CS324
+ * notes exercises 3 and 7; gradients: plain sums).  The kernels walk each
+ * item's list of tiles instead of scanning the mask.  Results are
+ * deterministic; they equal fa_forward_sparse / fa_backward_sparse's bit
+ * for bit when no row or column is split and to rounding otherwise.
+ *
+ * fa_sparse_schedule (host only; launches nothing): block_mask is a HOST
+ * int32 [nb, nb] array with fa_forward_sparse's meaning, nb = ceil(N/128).
+ * seg_tiles: the most tiles one item visits, >= 1, or 0 for the default
+ * max(8, ceil(B*H*(set tiles in reach) / 1024)).  Writes the number of ints
+ * the schedule takes to *needed_ints; writes the schedule itself only when
+ * `schedule` is non-NULL and schedule_ints >= that number (otherwise
+ * FA_ERR_NO_WORKSPACE; NULL schedule: FA_OK, size only).  The schedule
+ * depends on the mask, N, causal and seg only (B and H enter the default
+ * seg); its layout is the FA_SCHED_* header below followed by the items.
+ *
+ * fa_sparse_workspace_bytes: workspace of the balanced forward (backward =
+ * 0: partial O and LSE of the split rows) or backward (backward = 1: the
+ * workspace of fa_backward followed by the partial dQ, dK and dV of the
+ * split rows and columns); 0 for an invalid schedule or sizes, and 0 for a
+ * forward whose schedule splits nothing (workspace may then be NULL).
+ *
+ * fa_forward_sparse_balanced / fa_backward_sparse_balanced: as
+ * fa_forward_sparse / fa_backward_sparse, with `schedule` the host copy
+ * (read for the launch sizes and checked: FA_ERR_INVALID_ARG if it is not a
+ * schedule of this N and causal) and `schedule_dev` a device copy of the
+ * same ints (16-byte aligned; read by the kernels, which keep every access
+ * inside the sizes of the host copy's header, but a device copy that differs
+ * from the host copy gives undefined values).  FA_BF16 only.  Calls that
+ * share a workspace must not overlap.
+ */
+#define FA_SCHED_MAGIC 0
+#define FA_SCHED_HEADER_INTS 1
+#define FA_SCHED_NB 2
+#define FA_SCHED_CAUSAL 3
+#define FA_SCHED_SEG 4
+#define FA_SCHED_N_ROWS 5       /* row items (4 ints: tile, list offset, count, slot word) */
+#define FA_SCHED_N_COLS 6       /* column items */
+#define FA_SCHED_ROW_SLOTS 7    /* partial-result slots of split rows */
+#define FA_SCHED_COL_SLOTS 8
+#define FA_SCHED_N_LONG_ROWS 9  /* split rows (4 ints: tile, first slot, slots, 0) */
+#define FA_SCHED_N_LONG_COLS 10
+#define FA_SCHED_OFF_ROWS 11    /* int offsets of the sections */
+#define FA_SCHED_OFF_COLS 12
+#define FA_SCHED_OFF_LONG_ROWS 13
+#define FA_SCHED_OFF_LONG_COLS 14
+#define FA_SCHED_OFF_LISTS 15
+#define FA_SCHED_LIST_LEN 16
+#define FA_SCHED_TOTAL 17
+#define FA_SCHED_NNZ 18         /* set tiles in reach (causal: at or below the diagonal) */
+#define FA_SCHED_HEADER 20
+#define FA_SCHED_MAGIC_VALUE 0x46534221
+
+int fa_sparse_schedule(const int* block_mask, int N, int causal, int B, int H, int seg_tiles,
+                       int* schedule, size_t schedule_ints, size_t* needed_ints);
+
+size_t fa_sparse_workspace_bytes(const int* schedule, int B, int H, int N, int d, int backward);
+
+int fa_forward_sparse_balanced(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               const int* schedule, const int* schedule_dev, void* workspace,
+                               size_t workspace_bytes, int B, int H, int N, int d, float scale,
+                               int causal, int dtype, void* stream);
+
+int fa_backward_sparse_balanced(const void* Q, const void* K, const void* V, const void* O,
+                                const void* dO, const float* LSE, const int* schedule,
+                                const int* schedule_dev, void* dQ, void* dK, void* dV,
+                                void* workspace, size_t workspace_bytes, int B, int H, int N,
+                                int d, float scale, int causal, int dtype, void* stream);
+
+/*
  * Attention with dropout on the weights (the fused dropout of "FlashAttention
  * and GPU memory", section 07: applied after the softmax, before the product
  * with V).  No mask is stored: the forward keeps only the generator's key
