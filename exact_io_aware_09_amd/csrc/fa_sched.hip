@@ -108,6 +108,8 @@ void sum_parts_kernel(const float* __restrict__ part, const int* __restrict__ lo
   const int row = t * kTile + i;
   if (row >= N) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // (unrolled so that several loads are in flight; the sum stays in slot order)
+#pragma unroll 8
   for (int s = 0; s < ns; ++s) {
     const float4 v = *reinterpret_cast<const float4*>(
         part + (((size_t)(s0 + s) * BH + bh) * kTile + i) * D + 4 * lane4);
