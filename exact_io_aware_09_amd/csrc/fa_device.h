@@ -221,7 +221,15 @@ __device__ __forceinline__ int swz(int row) {
 // index (the low 3 bits select inside the 16-byte chunk).
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int col) {
-  return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
+  if constexpr (D > 128) {
+    // the swizzle (< 16) changes only the low 4 bits of the chunk index, so
+    // the chunks of columns 128 apart differ by a constant: written so, the
+    // offsets of a row's reads share 8 lane-dependent terms plus immediates
+    const int c = col >> 3;
+    return row * D + ((c & ~15) << 3) + (((c & 15) ^ swz<D>(row)) << 3) + (col & 7);
+  } else {
+    return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
+  }
 }
 
 // ds_read_b64_tr_b16: within each 16-lane group, output lane i receives

@@ -50,6 +50,29 @@ namespace {
 
 constexpr float kMaxWeight = 65536.0f;  // bound on one lane's share of a block's row sum
 
+#ifndef FA_FWD_QS_D256
+#define FA_FWD_QS_D256 1
+#endif
+#ifndef FA_FWD_FLA_D256
+#define FA_FWD_FLA_D256 0
+#endif
+// Scheduling groups for head dim 256 (0 = off; A > 0: the first A LDS reads
+// of the score and P.V sections go first, then one matrix instruction and
+// its reads alternate), so that A reads run ahead of the matrix instructions
+#ifndef FA_FWD_IGLP_D256
+#define FA_FWD_IGLP_D256 3
+#endif
+
+// Compiler fence for memory accesses: LDS reads after it are not scheduled
+// before it (it emits no instruction).
+__device__ __forceinline__ void read_fence() { asm volatile("" ::: "memory"); }
+
+// Extra kernel attributes (the head-dim-256 unit runs one wavefront per SIMD
+// and says so, which lets the scheduler use the whole register file)
+#ifndef FA_FWD_KERNEL_ATTR
+#define FA_FWD_KERNEL_ATTR
+#endif
+
 template <int D, int NW, int RB, int BC, int ST>
 struct FwdCfg {
   static constexpr int NT = NW * kWave;        // threads per workgroup
@@ -64,6 +87,16 @@ struct FwdCfg {
   // Q block staged through LDS (coalesced copy in, O out through the same
   // rows) when it fits in 16 KB; otherwise Q fragments load straight from HBM
   static constexpr bool QL = BR * D * 2 <= 16384;
+  // Q block kept in LDS for the whole kernel and its fragments read there
+  // for every K block, instead of held in VGPRs (head dim 256 at one
+  // workgroup per CU: the freed registers let the K and V fragment reads run
+  // ahead of the matrix instructions)
+  static constexpr bool QS = D >= 256 && FA_FWD_QS_D256;
+  static constexpr bool QST = QL || QS;  // Q staged through LDS (O leaves through it too)
+  // fragment reads issued ahead of their matrix instruction, held in place
+  // by compiler fences (0: left to the compiler, which for head dim 256
+  // issues each read right before its instruction and waits for it)
+  static constexpr int FLA = D >= 256 ? FA_FWD_FLA_D256 : 0;
   static_assert(ST >= 2 && ST <= 3, "two or three K/V stages");
 };
 
@@ -89,7 +122,7 @@ struct FwdCfg {
 // are scaled by 256 / t in the final division.
 template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL, bool SPLIT = false,
           bool SPARSE = false, bool DROP = false>
-__global__ __launch_bounds__(NW * 64, OCC)
+__global__ __launch_bounds__(NW * 64, OCC) FA_FWD_KERNEL_ATTR
 void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      const bf16_t* __restrict__ V, bf16_t* __restrict__ O,
                      float* __restrict__ LSE, int BH, int N, int nqb, int G, float c,
@@ -103,7 +136,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   __shared__ __attribute__((aligned(16))) bf16_t k0s[C::TILE], v0s[C::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t k1s[ST > 1 ? C::TILE : 8], v1s[ST > 1 ? C::TILE : 8];
   __shared__ __attribute__((aligned(16))) bf16_t k2s[ST > 2 ? C::TILE : 8], v2s[ST > 2 ? C::TILE : 8];
-  __shared__ __attribute__((aligned(16))) bf16_t qs[C::QL ? C::BR * D : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t qs[C::QST ? C::BR * D : 8];
   auto kst = [&](auto S) -> bf16_t* {
     if constexpr (decltype(S)::value == 0) return k0s;
     else if constexpr (decltype(S)::value == 1) return k1s;
@@ -198,8 +231,8 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   // The first K/V copies go out before Q is read, so that the latencies
   // overlap.
   fetch_at(jfirst, std::integral_constant<int, 0>{});
-  bf16x8 qf[RB][C::KSTEPS];  // B operands of S^T = K Q^T (lane = query row)
-  if constexpr (C::QL) {
+  bf16x8 qf[RB][C::QS ? 1 : C::KSTEPS];  // B operands of S^T = K Q^T (lane = query row)
+  if constexpr (C::QST) {
     // Q block copied row-major (coalesced) into LDS, rows past N as zeros
     dma_tile<D, C::BR, C::NT>(make_copy_rsrc(Q + hoff, head_bytes), q0, qs, tid);
   } else {
@@ -251,19 +284,58 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   // S^T = K Q^T for the block at key j0 (lane: query; registers: keys), each
   // K fragment feeding the RB row blocks; causal-future keys and keys past
   // the end become -inf, on the blocks that need it only.
+  // Q fragment (row block rb, k-step s): held in VGPRs, or read from the
+  // wavefront's rows of the Q tile in LDS
+  auto qfrag = [&](int rb, int s) -> bf16x8 {
+    if constexpr (C::QS) return frag_rows<D>(qs, w * C::RW + 32 * rb, 16 * s, c32, h);
+    else return qf[rb][s];
+  };
   auto scores = [&](const bf16_t* Ks, int j0, f32x16 (&sacc)[RB][C::KB]) {
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
+    for (int kb = 0; kb < C::KB; ++kb) if constexpr (C::FLA > 0) {
+      constexpr int W = C::FLA + 1;
+      bf16x8 kw[W], qw[W][RB];
+      const f32x16 z = {};
+#pragma unroll
+      for (int s = 0; s < C::FLA && s < C::KSTEPS; ++s) {
+        kw[s] = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) qw[s][rb] = qfrag(rb, s);
+      }
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        if (s + C::FLA < C::KSTEPS) {
+          kw[(s + C::FLA) % W] = frag_rows<D>(Ks, kb * 32, 16 * (s + C::FLA), c32, h);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) qw[(s + C::FLA) % W][rb] = qfrag(rb, s + C::FLA);
+        }
+        read_fence();
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          sacc[rb][kb] = mfma32x32x16(kw[s % W], qw[s % W][rb], s == 0 ? z : sacc[rb][kb]);
+      }
+    } else {
       bf16x8 kfr[C::KSTEPS];
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) kfr[s] = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
       const f32x16 z = {};
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[0], qf[rb][0], z);
+      for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[0], qfrag(rb, 0), z);
 #pragma unroll
       for (int s = 1; s < C::KSTEPS; ++s)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[s], qf[rb][s], sacc[rb][kb]);
+        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[s], qfrag(rb, s), sacc[rb][kb]);
+      if constexpr (D >= 256 && FA_FWD_IGLP_D256 > 0) {
+        // reads per matrix instruction: K, plus Q when Q stays in LDS
+        constexpr int RPM = C::QS ? 2 : 1, A = FA_FWD_IGLP_D256;
+        __builtin_amdgcn_sched_group_barrier(0x100, A * RPM, 0);
+#pragma unroll
+        for (int i = 0; i < C::KSTEPS - A; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
+      }
     }
     const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
     if (need_mask) {
@@ -388,21 +460,60 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
       // P^T as B operand (k-step u: registers 8*(u&1).. of key block u>>1,
       // i.e. keys 16u + 8*(e>>2) + 4h + (e&3)), rounded to bf16, then
       // O^T += V^T P^T with each V fragment feeding the RB row blocks.
+      if constexpr (C::FLA > 0) {
+        bf16x8 pf[C::PU][RB];
 #pragma unroll
-      for (int u = 0; u < C::PU; ++u) {
-        bf16x8 pf[RB];
+        for (int u = 0; u < C::PU; ++u)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const f32x16& pv = sacc[rb][u >> 1];
-          const int r0 = 8 * (u & 1);
-          pf[rb] = bf16x8_from(pack_bf16x2(pv[r0], pv[r0 + 1]), pack_bf16x2(pv[r0 + 2], pv[r0 + 3]),
-                               pack_bf16x2(pv[r0 + 4], pv[r0 + 5]), pack_bf16x2(pv[r0 + 6], pv[r0 + 7]));
+          for (int rb = 0; rb < RB; ++rb) {
+            const f32x16& pv = sacc[rb][u >> 1];
+            const int r0 = 8 * (u & 1);
+            pf[u][rb] = bf16x8_from(pack_bf16x2(pv[r0], pv[r0 + 1]), pack_bf16x2(pv[r0 + 2], pv[r0 + 3]),
+                                    pack_bf16x2(pv[r0 + 4], pv[r0 + 5]), pack_bf16x2(pv[r0 + 6], pv[r0 + 7]));
+          }
+        constexpr int W = C::FLA + 1, NV = C::PU * C::DB;
+        bf16x8 vw[W];
+#pragma unroll
+        for (int i = 0; i < C::FLA && i < NV; ++i) vw[i] = frag_tr<D>(Vs, 16 * (i / C::DB), (i % C::DB) * 32, lane);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          if (i + C::FLA < NV) {
+            const int n = i + C::FLA;
+            vw[n % W] = frag_tr<D>(Vs, 16 * (n / C::DB), (n % C::DB) * 32, lane);
+          }
+          read_fence();
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            oacc[rb][i % C::DB] = mfma32x32x16(vw[i % W], pf[i / C::DB][rb], oacc[rb][i % C::DB]);
         }
+      } else {
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 vfr = frag_tr<D>(Vs, 16 * u, db * 32, lane);
+        for (int u = 0; u < C::PU; ++u) {
+          bf16x8 pf[RB];
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32x32x16(vfr, pf[rb], oacc[rb][db]);
+          for (int rb = 0; rb < RB; ++rb) {
+            const f32x16& pv = sacc[rb][u >> 1];
+            const int r0 = 8 * (u & 1);
+            pf[rb] = bf16x8_from(pack_bf16x2(pv[r0], pv[r0 + 1]), pack_bf16x2(pv[r0 + 2], pv[r0 + 3]),
+                                 pack_bf16x2(pv[r0 + 4], pv[r0 + 5]), pack_bf16x2(pv[r0 + 6], pv[r0 + 7]));
+          }
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const bf16x8 vfr = frag_tr<D>(Vs, 16 * u, db * 32, lane);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32x32x16(vfr, pf[rb], oacc[rb][db]);
+          }
+        }
+        if constexpr (D >= 256 && FA_FWD_IGLP_D256 > 0) {
+          // two transpose reads per V fragment
+          constexpr int A = FA_FWD_IGLP_D256, NV = C::PU * C::DB;
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * A, 0);
+#pragma unroll
+          for (int i = 0; i < NV - A; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
         }
       }
     }
@@ -493,7 +604,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     const int query = q0w + 32 * rb + c32;
     const float lt = sum_halves(l[rb]);  // >= 1: the row maximum has weight >= 1
     const float inv = DROP ? __builtin_amdgcn_rcpf(lt) * dr.scale : __builtin_amdgcn_rcpf(lt);
-    if constexpr (C::QL) {
+    if constexpr (C::QST) {
       // O fragment (dims db*32 + 8g + 4h + 0..3 of this lane's row) into
       // this wavefront's rows of the Q staging tile
 #pragma unroll
@@ -518,7 +629,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     }
     if (h == 0 && query < N) LSE[(size_t)bh * N + query] = (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2;
   }
-  if constexpr (C::QL) {
+  if constexpr (C::QST) {
     // rows back out of LDS as whole 16-byte chunks: 8 lanes per row, so each
     // store instruction writes 8 complete rows
     constexpr int CPR = D / 8;
