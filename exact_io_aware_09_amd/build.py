@@ -24,14 +24,15 @@ LIB_PATH = PKG_DIR / LIB_NAME
 BUILD_DIR = REPO_DIR / "_build"
 ARCH = "gfx950"
 # Matrix instructions with their accumulators in VGPRs: for the head-dim-256
-# units and the non-causal head-dim-128 backward, whose kernels run one
-# wavefront per SIMD (see fa_fwd_d256.hip, fa_bwd_d128nc.hip).
+# backward and FP8 units and the non-causal head-dim-128 backward, whose
+# kernels run one wavefront per SIMD (see fa_bwd_d256.hip, fa_bwd_d128nc.hip;
+# the head-dim-256 forward keeps its accumulator in AGPRs, fa_fwd_d256.hip).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 # (unit, extra flags)
 UNITS = [
     ("fa_api.hip", []),
     ("fa_fwd.hip", []),
-    ("fa_fwd_d256.hip", VGPR_FORM),
+    ("fa_fwd_d256.hip", []),
     ("fa_bwd.hip", []),
     ("fa_bwd_d256.hip", VGPR_FORM),
     ("fa_bwd_d128nc.hip", VGPR_FORM),

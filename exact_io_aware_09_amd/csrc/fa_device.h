@@ -383,6 +383,22 @@ __device__ __forceinline__ void dma_tile(copy_rsrc r, int r0, bf16_t* tile, int 
   }
 }
 
+// The same copy, without the compiler memory clobber: for copies into a
+// stage that nothing reads until the next ring barrier (whose asm statement
+// does clobber memory), so that the compiler may keep scheduling LDS reads
+// of other stages around it.
+__device__ __forceinline__ void lds_copy16_free(copy_rsrc r, uint32_t voff, uint32_t lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(r));
+}
+
 // Copy of `ROWS` (<= 64) consecutive floats starting at row r0 of a float
 // vector into LDS (lane L -> dst[L]; lanes past ROWS repeat rows, so dst
 // must hold 64 floats; rows past the descriptor's end read as 0).  One copy

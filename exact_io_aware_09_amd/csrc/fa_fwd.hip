@@ -50,28 +50,60 @@ namespace {
 
 constexpr float kMaxWeight = 65536.0f;  // bound on one lane's share of a block's row sum
 
-#ifndef FA_FWD_QS_D256
-#define FA_FWD_QS_D256 1
-#endif
-#ifndef FA_FWD_FLA_D256
-#define FA_FWD_FLA_D256 0
-#endif
-// Scheduling groups for head dim 256 (0 = off; A > 0: the first A LDS reads
-// of the score and P.V sections go first, then one matrix instruction and
-// its reads alternate), so that A reads run ahead of the matrix instructions
+// Head dim 256 (one wavefront per SIMD, so the order of a wavefront's own
+// instructions decides how much overlaps):
+//  * FA_FWD_IGLP_D256: K fragment reads issued that many matrix instructions
+//    ahead of their use (V fragments: FA_FWD_PIPE_VA);
+//  * FA_FWD_PIPE_D256: software-pipelined loop (the P.V product of block t-1
+//    runs on the matrix cores while the softmax of block t runs on the
+//    vector ALU);
+//  * FA_FWD_DMA_GAP: matrix instructions between two of a step's K/V copies.
 #ifndef FA_FWD_IGLP_D256
-#define FA_FWD_IGLP_D256 3
+#define FA_FWD_IGLP_D256 5
+#endif
+#ifndef FA_FWD_PIPE_D256
+#define FA_FWD_PIPE_D256 1
+#endif
+#ifndef FA_FWD_PIPE_VA
+#define FA_FWD_PIPE_VA 5
+#endif
+#ifndef FA_FWD_DMA_GAP
+#define FA_FWD_DMA_GAP 2
 #endif
 
-// Compiler fence for memory accesses: LDS reads after it are not scheduled
-// before it (it emits no instruction).
-__device__ __forceinline__ void read_fence() { asm volatile("" ::: "memory"); }
-
-// Extra kernel attributes (the head-dim-256 unit runs one wavefront per SIMD
-// and says so, which lets the scheduler use the whole register file)
-#ifndef FA_FWD_KERNEL_ATTR
-#define FA_FWD_KERNEL_ATTR
+// Output accumulator rescaled in place in AGPRs (units compiled with the
+// matrix instructions in their AGPR form): keeps the accumulator's registers
+// AGPRs across the loop, instead of a VGPR copy that the compiler would
+// otherwise make at every step to share one register class with the rare
+// rescale.
+#ifndef FA_FWD_ACC_AGPR
+#define FA_FWD_ACC_AGPR 0
 #endif
+
+// acc *= s on an accumulator held in AGPRs.  The first statement waits out
+// the matrix-instruction result latency itself (the compiler does not track
+// hazards inside asm), the last one gives the writes time to settle before a
+// matrix instruction reads them.
+__device__ __forceinline__ void scale_acc_agpr(f32x16& acc, float s) {
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = acc[r];
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "s_nop 0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(x[r]), "=&v"(t)
+        : "v"(s));
+  }
+  asm volatile("s_nop 4" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = x[r];
+}
 
 template <int D, int NW, int RB, int BC, int ST>
 struct FwdCfg {
@@ -86,17 +118,13 @@ struct FwdCfg {
   static constexpr int DMA_PER_TILE = TILE / 8 / NT;  // loads per tile per lane
   // Q block staged through LDS (coalesced copy in, O out through the same
   // rows) when it fits in 16 KB; otherwise Q fragments load straight from HBM
+  // (the Q fragments stay in VGPRs either way)
   static constexpr bool QL = BR * D * 2 <= 16384;
-  // Q block kept in LDS for the whole kernel and its fragments read there
-  // for every K block, instead of held in VGPRs (head dim 256 at one
-  // workgroup per CU: the freed registers let the K and V fragment reads run
-  // ahead of the matrix instructions)
-  static constexpr bool QS = D >= 256 && FA_FWD_QS_D256;
-  static constexpr bool QST = QL || QS;  // Q staged through LDS (O leaves through it too)
-  // fragment reads issued ahead of their matrix instruction, held in place
-  // by compiler fences (0: left to the compiler, which for head dim 256
-  // issues each read right before its instruction and waits for it)
-  static constexpr int FLA = D >= 256 ? FA_FWD_FLA_D256 : 0;
+  static constexpr bool QST = QL;
+  // software-pipelined loop (head dim 256 at one wavefront per SIMD, where no
+  // other wavefront fills the matrix cores during a softmax)
+  static constexpr bool PIPE = D >= 256 && FA_FWD_PIPE_D256 && RB == 1 && KB == 1 && DMA_PER_TILE == 4 &&
+                               KSTEPS == 16 && PU == 2;
   static_assert(ST >= 2 && ST <= 3, "two or three K/V stages");
 };
 
@@ -122,13 +150,14 @@ struct FwdCfg {
 // are scaled by 256 / t in the final division.
 template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL, bool SPLIT = false,
           bool SPARSE = false, bool DROP = false>
-__global__ __launch_bounds__(NW * 64, OCC) FA_FWD_KERNEL_ATTR
+__global__ __launch_bounds__(NW * 64, OCC)
 void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      const bf16_t* __restrict__ V, bf16_t* __restrict__ O,
                      float* __restrict__ LSE, int BH, int N, int nqb, int G, float c,
                      SplitArgs sa = {}, SparseArgs sp = {}, DropArgs dr = {}) {
   using C = FwdCfg<D, NW, RB, BC, ST>;
   static_assert((int)SPLIT + (int)SPARSE + (int)DROP <= 1, "one variant at a time");
+  constexpr bool PIPE = C::PIPE && !SPARSE;
   static_assert(!SPARSE || (ST == 2 && C::BR == 128), "sparse walk: two stages, 128-row query blocks");
   // One LDS variable per stage and operand: with the stage a compile-time
   // constant at every access, the compiler can tell the block being read
@@ -230,8 +259,9 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   auto fetch = [&](int t, auto S) { fetch_at(kbase + t * BC, S); };
   // The first K/V copies go out before Q is read, so that the latencies
   // overlap.
-  fetch_at(jfirst, std::integral_constant<int, 0>{});
-  bf16x8 qf[RB][C::QS ? 1 : C::KSTEPS];  // B operands of S^T = K Q^T (lane = query row)
+  if constexpr (PIPE) dma_tile<D, BC, C::NT>(rk, jfirst, k0s, tid);
+  else fetch_at(jfirst, std::integral_constant<int, 0>{});
+  bf16x8 qf[RB][C::KSTEPS];  // B operands of S^T = K Q^T (lane = query row)
   if constexpr (C::QST) {
     // Q block copied row-major (coalesced) into LDS, rows past N as zeros
     dma_tile<D, C::BR, C::NT>(make_copy_rsrc(Q + hoff, head_bytes), q0, qs, tid);
@@ -251,10 +281,23 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) pin_ready(qf[rb][s]);
   }
-  if constexpr (ST > 2) {
-    if (1 < ntiles) fetch(1, std::integral_constant<int, 1>{});
+  if constexpr (PIPE) {
+    // pipelined loop: K of blocks 0..ST-2 and V of blocks 0..ST-3 before
+    // step 0; K of block 0 (and Q) resident, the rest may stay in flight
+    if constexpr (ST > 2) {
+      const bool k1 = 1 < ntiles;
+      if (k1) dma_tile<D, BC, C::NT>(rk, jfirst + BC, k1s, tid);
+      dma_tile<D, BC, C::NT>(rv, jfirst, v0s, tid);
+      wait_vmem_tiles<C::DMA_PER_TILE, 2>((int)k1 + 1);
+    } else {
+      wait_vmem_le<0>();
+    }
+  } else {
+    if constexpr (ST > 2) {
+      if (1 < ntiles) fetch(1, std::integral_constant<int, 1>{});
+    }
+    wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - 1));
   }
-  wait_vmem_tiles<2 * C::DMA_PER_TILE, ST - 2>(min(ST - 2, ntiles - 1));
   ring_barrier();
   if constexpr (C::QL) {
     // each wavefront reads (and later overwrites with O) only its own rows
@@ -284,55 +327,28 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   // S^T = K Q^T for the block at key j0 (lane: query; registers: keys), each
   // K fragment feeding the RB row blocks; causal-future keys and keys past
   // the end become -inf, on the blocks that need it only.
-  // Q fragment (row block rb, k-step s): held in VGPRs, or read from the
-  // wavefront's rows of the Q tile in LDS
-  auto qfrag = [&](int rb, int s) -> bf16x8 {
-    if constexpr (C::QS) return frag_rows<D>(qs, w * C::RW + 32 * rb, 16 * s, c32, h);
-    else return qf[rb][s];
-  };
   auto scores = [&](const bf16_t* Ks, int j0, f32x16 (&sacc)[RB][C::KB]) {
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) if constexpr (C::FLA > 0) {
-      constexpr int W = C::FLA + 1;
-      bf16x8 kw[W], qw[W][RB];
-      const f32x16 z = {};
-#pragma unroll
-      for (int s = 0; s < C::FLA && s < C::KSTEPS; ++s) {
-        kw[s] = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) qw[s][rb] = qfrag(rb, s);
-      }
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
-        if (s + C::FLA < C::KSTEPS) {
-          kw[(s + C::FLA) % W] = frag_rows<D>(Ks, kb * 32, 16 * (s + C::FLA), c32, h);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) qw[(s + C::FLA) % W][rb] = qfrag(rb, s + C::FLA);
-        }
-        read_fence();
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          sacc[rb][kb] = mfma32x32x16(kw[s % W], qw[s % W][rb], s == 0 ? z : sacc[rb][kb]);
-      }
-    } else {
+    for (int kb = 0; kb < C::KB; ++kb) {
       bf16x8 kfr[C::KSTEPS];
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) kfr[s] = frag_rows<D>(Ks, kb * 32, 16 * s, c32, h);
       const f32x16 z = {};
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[0], qfrag(rb, 0), z);
+      for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[0], qf[rb][0], z);
 #pragma unroll
       for (int s = 1; s < C::KSTEPS; ++s)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[s], qfrag(rb, s), sacc[rb][kb]);
+        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32x32x16(kfr[s], qf[rb][s], sacc[rb][kb]);
       if constexpr (D >= 256 && FA_FWD_IGLP_D256 > 0) {
-        // reads per matrix instruction: K, plus Q when Q stays in LDS
-        constexpr int RPM = C::QS ? 2 : 1, A = FA_FWD_IGLP_D256;
-        __builtin_amdgcn_sched_group_barrier(0x100, A * RPM, 0);
+        // scheduling groups: the first A K reads, then one matrix
+        // instruction and one read alternate, so that A reads stay ahead
+        constexpr int A = FA_FWD_IGLP_D256;
+        __builtin_amdgcn_sched_group_barrier(0x100, A, 0);
 #pragma unroll
         for (int i = 0; i < C::KSTEPS - A; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
       }
@@ -435,7 +451,13 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+              for (int r = 0; r < 16; ++r) {
+                if constexpr (FA_FWD_ACC_AGPR && D >= 256) {
+                  if (r == 0) scale_acc_agpr(oacc[rb][db], alpha);
+                } else {
+                  oacc[rb][db][r] *= alpha;
+                }
+              }
           }
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb) sacc[rb][kb] = s2[rb][kb];
@@ -460,33 +482,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
       // P^T as B operand (k-step u: registers 8*(u&1).. of key block u>>1,
       // i.e. keys 16u + 8*(e>>2) + 4h + (e&3)), rounded to bf16, then
       // O^T += V^T P^T with each V fragment feeding the RB row blocks.
-      if constexpr (C::FLA > 0) {
-        bf16x8 pf[C::PU][RB];
-#pragma unroll
-        for (int u = 0; u < C::PU; ++u)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const f32x16& pv = sacc[rb][u >> 1];
-            const int r0 = 8 * (u & 1);
-            pf[u][rb] = bf16x8_from(pack_bf16x2(pv[r0], pv[r0 + 1]), pack_bf16x2(pv[r0 + 2], pv[r0 + 3]),
-                                    pack_bf16x2(pv[r0 + 4], pv[r0 + 5]), pack_bf16x2(pv[r0 + 6], pv[r0 + 7]));
-          }
-        constexpr int W = C::FLA + 1, NV = C::PU * C::DB;
-        bf16x8 vw[W];
-#pragma unroll
-        for (int i = 0; i < C::FLA && i < NV; ++i) vw[i] = frag_tr<D>(Vs, 16 * (i / C::DB), (i % C::DB) * 32, lane);
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          if (i + C::FLA < NV) {
-            const int n = i + C::FLA;
-            vw[n % W] = frag_tr<D>(Vs, 16 * (n / C::DB), (n % C::DB) * 32, lane);
-          }
-          read_fence();
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            oacc[rb][i % C::DB] = mfma32x32x16(vw[i % W], pf[i / C::DB][rb], oacc[rb][i % C::DB]);
-        }
-      } else {
+      {
 #pragma unroll
         for (int u = 0; u < C::PU; ++u) {
           bf16x8 pf[RB];
@@ -523,7 +519,232 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
       ring_barrier();
     }
   };
-  if constexpr (SPARSE) {
+  if constexpr (PIPE) {
+    // Software pipeline.  Step t computes the scores of block t, then its
+    // softmax on the vector ALU interleaved with O^T += V^T P^T of block t-1
+    // on the matrix cores (one wavefront per SIMD: nothing else would fill
+    // the matrix cores during the softmax).  Step t copies in K of block
+    // t+ST-1 and V of block t+ST-2: the K ring holds blocks t..t+ST-1 and
+    // the V ring blocks t-1..t+ST-2, each block in stage (block mod ST).
+    // Causal steps are active up to the wavefront's diagonal and inactive
+    // after it, so an active step always has the previous block's P.V
+    // pending.
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2 % ST>;
+    bf16x8 pp[C::PU];  // P^T of the previous block, B operands of V^T P^T
+    bool pend = false;
+    auto pv = [&](const bf16_t* Vs) {
+#pragma unroll
+      for (int u = 0; u < C::PU; ++u)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+          oacc[0][db] = mfma32x32x16(frag_tr<D>(Vs, 16 * u, db * 32, lane), pp[u], oacc[0][db]);
+    };
+    // Copy plan of the ring: copy i of a [BC x D] tile takes LDS block
+    // w + i*NWAVE of the stage (1 KB, lane L its 16 bytes at 16 L) from the
+    // global chunk the swizzle places there; its per-lane byte offset for
+    // row 0 and its LDS offset are fixed for the whole kernel.
+    constexpr int NWAVE = NW;
+    uint32_t cvo[C::DMA_PER_TILE], clo[C::DMA_PER_TILE];
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_TILE; ++i) {
+      const int blk = w + i * NWAVE;
+      const int pos = blk * 64 + lane;
+      const int row = pos / (D / 8), cc = (pos % (D / 8)) ^ swz<D>(row);
+      cvo[i] = ((uint32_t)row * D + cc * 8) * 2u;
+      clo[i] = __builtin_amdgcn_readfirstlane((uint32_t)blk * 1024u);
+    }
+    const uint32_t lk[3] = {lds_address(k0s), lds_address(k1s), lds_address(k2s)};
+    const uint32_t lv[3] = {lds_address(v0s), lds_address(v1s), lds_address(v2s)};
+    // copy i of block r0's K (V) tile into stage st
+    auto copy_k = [&](int r0, int st, int i) {
+      lds_copy16_free(rk, cvo[i] + (uint32_t)r0 * (uint32_t)(D * 2), lk[st] + clo[i]);
+    };
+    auto copy_v = [&](int r0, int st, int i) {
+      lds_copy16_free(rv, cvo[i] + (uint32_t)r0 * (uint32_t)(D * 2), lv[st] + clo[i]);
+    };
+    // keeps the matrix instructions and the copies in program order (vector
+    // and scalar ALU instructions may still move across)
+    auto pin = [] { __builtin_amdgcn_sched_barrier(0x406); };
+    auto pstep = [&](int t, auto S, auto FIRST) {
+      constexpr int s = decltype(S)::value;
+      constexpr bool first = decltype(FIRST)::value;
+      constexpr int sk = (s + ST - 1) % ST;  // stage of K(t+ST-1), and of V(t-1)
+      constexpr int sv = (s + ST - 2) % ST;  // stage of V(t+ST-2)
+      const int j0 = kbase + t * BC;
+      const bool kf = t + ST - 1 < ntiles, vf = t + ST - 2 < ntiles;
+      const bf16_t* Ks = kst(S);
+      const bf16_t* Vp = vst(std::integral_constant<int, sk>{});  // V of block t-1
+      const bool active = !CAUSAL || j0 <= q0w + C::RW - 1;
+      // Main path (active steps after the first): the copies are spread
+      // over the score section, one after every FA_FWD_DMA_GAP-th matrix
+      // instruction.  Each copy holds up the wavefront's issue until the
+      // texture unit takes it, which a burst at the start of the step turns
+      // into a stall of all four wavefronts.  There they are issued
+      // unconditionally: a copy past the last block reads rows past the
+      // range (zeros) or rows it does not need, into a stage that is not
+      // read again.
+      constexpr bool spread = !first;
+      auto copy_part = [&](int i) {  // copies 0..3: K of block t+ST-1; 4..7: V of block t+ST-2
+        if (i < C::DMA_PER_TILE) copy_k(j0 + (ST - 1) * BC, sk, i);
+        else copy_v(j0 + (ST - 2) * BC, sv, i - C::DMA_PER_TILE);
+      };
+      if (!spread || !active) {
+        if (kf) dma_tile<D, BC, C::NT>(rk, j0 + (ST - 1) * BC, kst(std::integral_constant<int, sk>{}), tid);
+        if (vf) dma_tile<D, BC, C::NT>(rv, j0 + (ST - 2) * BC, vst(std::integral_constant<int, sv>{}), tid);
+      }
+      if (active) {
+        f32x16 sacc[RB][C::KB];
+        if constexpr (spread) {
+          // S^T = K Q^T written in issue order: K fragment reads A ahead,
+          // copies between the matrix instructions
+          constexpr int A = FA_FWD_IGLP_D256 > 0 ? FA_FWD_IGLP_D256 : 3, W = A + 1;
+          bf16x8 kw[W];
+#pragma unroll
+          for (int i = 0; i < A; ++i) kw[i] = frag_rows<D>(Ks, 0, 16 * i, c32, h);
+          const f32x16 z = {};
+#pragma unroll
+          for (int i = 0; i < C::KSTEPS; ++i) {
+            if (i + A < C::KSTEPS) kw[(i + A) % W] = frag_rows<D>(Ks, 0, 16 * (i + A), c32, h);
+            sacc[0][0] = mfma32x32x16(kw[i % W], qf[0][i], i == 0 ? z : sacc[0][0]);
+            if (i % FA_FWD_DMA_GAP == 0 && i / FA_FWD_DMA_GAP < 2 * C::DMA_PER_TILE) {
+              pin();
+              copy_part(i / FA_FWD_DMA_GAP);
+              pin();
+            }
+          }
+          const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
+          if (need_mask) {
+            keep_branch();
+            const int nk = N - j0 - 4 * h;
+            const int kq = j0 + 4 * h - (q0w + c32);
+            const int lim = CAUSAL ? min(-kq, nk - 1) : nk - 1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (8 * (r >> 2) + (r & 3) > lim) sacc[0][0][r] = -INFINITY;
+          }
+        } else {
+          scores(Ks, j0, sacc);
+        }
+        float rs[RB];
+        if constexpr (first) {
+          m[0] = block_max(sacc[0]);
+          rs[0] = exponentiate(sacc[0], base(m[0]));
+        } else {
+          {
+            // written in issue order: V fragment reads A ahead, then each
+            // matrix instruction followed by one score's exponential
+            constexpr int A = FA_FWD_PIPE_VA, NV = C::PU * C::DB, W = A + 1;
+            const float mb = base(m[0]);
+            bf16x8 vw[W];
+#pragma unroll
+            for (int i = 0; i < A; ++i) vw[i] = frag_tr<D>(Vp, 16 * (i / C::DB), (i % C::DB) * 32, lane);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+              if (i + A < NV) {
+                const int n = i + A;
+                vw[n % W] = frag_tr<D>(Vp, 16 * (n / C::DB), (n % C::DB) * 32, lane);
+              }
+              oacc[0][i % C::DB] = mfma32x32x16(vw[i % W], pp[i / C::DB], oacc[0][i % C::DB]);
+              sacc[0][0][i] = fast_exp2(fmaf(sacc[0][0][i], c, -mb));
+              if constexpr (spread) {
+                // the copies that did not fit in the score section
+                constexpr int NS = (C::KSTEPS + FA_FWD_DMA_GAP - 1) / FA_FWD_DMA_GAP;
+                if (NS + (i - 2) / 3 < 2 * C::DMA_PER_TILE && i >= 2 && (i - 2) % 3 == 0) {
+                  pin();
+                  copy_part(NS + (i - 2) / 3);
+                  pin();
+                }
+              }
+            }
+            float part[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) part[r] = sacc[0][0][2 * r] + sacc[0][0][2 * r + 1];
+#pragma unroll
+            for (int n = 8; n > 1; n /= 2)
+#pragma unroll
+              for (int i = 0; i < n / 2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
+            rs[0] = part[0];
+          }
+        }
+        if (wave_any(!(rs[0] <= kMaxWeight))) {
+          // a row broke the bound: as in the plain loop (O already holds
+          // block t-1, so the rescale covers it)
+          keep_branch();
+          f32x16 s2[RB][C::KB];
+          scores(Ks, j0, s2);
+          const bool own = !(rs[0] <= kMaxWeight);
+          const bool row = max_halves(own ? 1.f : 0.f) > 0.f;
+          const float mx = block_max(s2[0]);
+          if (row) {
+            const float alpha = fast_exp2(m[0] - mx);
+            m[0] = mx;
+            l[0] *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                if constexpr (FA_FWD_ACC_AGPR) {
+                  if (r == 0) scale_acc_agpr(oacc[0][db], alpha);
+                } else {
+                  oacc[0][db][r] *= alpha;
+                }
+              }
+          }
+          sacc[0][0] = s2[0][0];
+          rs[0] = exponentiate(sacc[0], base(m[0]));
+        }
+        l[0] += rs[0];
+        if constexpr (DROP) {
+          uint32_t dw[4];
+          draws_query_cols(q0w, j0, bh, lane, dr.k0, dr.k1, dw);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!kept(dw, r, dr.thresh)) sacc[0][0][r] = 0.f;
+        }
+        // k-step u of V^T P^T: registers 8u.. of the block (keys 16u + 8*(e>>2) + 4h + (e&3))
+#pragma unroll
+        for (int u = 0; u < C::PU; ++u) {
+          const f32x16& pv_ = sacc[0][0];
+          const int r0 = 8 * u;
+          pp[u] = bf16x8_from(pack_bf16x2(pv_[r0], pv_[r0 + 1]), pack_bf16x2(pv_[r0 + 2], pv_[r0 + 3]),
+                              pack_bf16x2(pv_[r0 + 4], pv_[r0 + 5]), pack_bf16x2(pv_[r0 + 6], pv_[r0 + 7]));
+        }
+        pend = true;
+      } else if (pend) {
+        pv(Vp);
+        pend = false;
+      }
+      // K of block t+1 and V of block t resident (this step's copies may
+      // stay in flight); the stages read in this step are free
+      if constexpr (ST == 2) wait_vmem_le<0>();
+      else wait_vmem_tiles<C::DMA_PER_TILE, 2>((int)kf + (int)vf);
+      ring_barrier();
+    };
+    pstep(0, S0{}, std::true_type{});
+    for (int t = 1; t < ntiles; t += ST) {
+      pstep(t, S1{}, std::false_type{});
+      if (t + 1 < ntiles) pstep(t + 1, S2{}, std::false_type{});
+      if constexpr (ST > 2) {
+        if (t + 2 < ntiles) pstep(t + 2, S0{}, std::false_type{});
+      }
+    }
+    if (pend) {
+      // P.V of the last block
+      const int sl = (ntiles - 1) % ST;
+      if (sl == 0) {
+        pv(v0s);
+      } else {
+        if constexpr (ST > 2) {
+          if (sl == 2) pv(v2s);
+          else pv(v1s);
+        } else {
+          pv(v1s);
+        }
+      }
+    }
+  } else if constexpr (SPARSE) {
     int j0 = jfirst, jn = walk.next(j0);
     for (int t = 0;; t += 2) {
       step(t, j0, jn, std::integral_constant<int, 0>{});
@@ -656,8 +877,8 @@ hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* 
   const int G = head_group(OCC * 4 / NW, nqb);
   if (sp.on()) {
     // the sparse walk takes 128-row query blocks in two stages
-    if constexpr (C::BR == 128 && ST == 2)
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, true>), dim3((unsigned)grid),
+    if constexpr (C::BR == 128)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, 2, OCC, CAUSAL, false, true>), dim3((unsigned)grid),
                          dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                          (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, sp);
     else

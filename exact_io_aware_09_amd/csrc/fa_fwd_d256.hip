@@ -1,11 +1,15 @@
-// fa_fwd_d256.hip -- head-dim-256 instantiations of the forward (plain, key-split, dropout) kernels.
+// fa_fwd_d256.hip -- head-dim-256 instantiations of the forward (plain, key-split, dropout,
+// block-sparse) kernels.
 //
 // The source is fa_fwd.hip itself, compiled a second time with only its
-// head-dim-256 launchers, and with the matrix instructions selected in their
-// VGPR form (the build passes -mllvm -amdgpu-mfma-vgpr-form for this unit).
-// At one wavefront per SIMD the default selection puts the accumulators in
-// AGPRs and the compiler then copies the whole output accumulator between
-// AGPRs and VGPRs on every loop iteration (and spills in the backward); the
-// VGPR form removes those copies.  Head dims 64 and 128 keep the default.
+// head-dim-256 launchers.  These kernels run one wavefront per SIMD with the
+// whole register file: the output accumulator (128 registers per lane) lives
+// in AGPRs, the matrix instructions' default form, which leaves the VGPRs to
+// the Q fragments (64 registers, read from there for every K block instead
+// of from LDS) and the fragments in flight.  The rare rescale of the
+// accumulator is done in place in the AGPRs (FA_FWD_ACC_AGPR): were it done
+// on VGPR copies, the compiler would give the accumulator one register class
+// for the whole loop and copy it between AGPRs and VGPRs at every step.
 #define FA_D256_UNIT 1
+#define FA_FWD_ACC_AGPR 1
 #include "fa_fwd.hip"

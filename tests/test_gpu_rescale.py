@@ -136,33 +136,37 @@ def test_fp32_moving_maximum(shape, pattern, causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("pattern", PATTERNS)
-def test_split_forward_moving_maximum(pattern, causal):
-    shape = (1, 2, 700, 64)
+@pytest.mark.parametrize("shape", [(1, 2, 700, 64), (1, 1, 700, 256)])
+def test_split_forward_moving_maximum(shape, pattern, causal):
+    scale = 1.0 / math.sqrt(shape[3])
     q, k, v, _ = make_trending_inputs(shape, torch.bfloat16, 80, pattern, 150.0)
     qd, kd, vd = (t.to(dev()) for t in (q, k, v))
-    o, lse = fa.forward_split(qd, kd, vd, 0.125, causal, splits=4)
+    o, lse = fa.forward_split(qd, kd, vd, scale, causal, splits=4)
     torch.cuda.synchronize()
-    ro, rl = A.per_head(A.attention_forward, (q, k, v), 0.125, causal)
-    what = f"{pattern} causal={causal}"
+    ro, rl = A.per_head(A.attention_forward, (q, k, v), scale, causal)
+    what = f"{shape} {pattern} causal={causal}"
     assert max_abs(o.cpu(), ro) <= 2e-2, f"{what}: O {max_abs(o.cpu(), ro)}"
     assert max_abs(lse.cpu(), rl) <= 1e-3, f"{what}: LSE {max_abs(lse.cpu(), rl)}"
 
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("pattern", PATTERNS)
-def test_dropout_forward_moving_maximum(pattern, causal):
+@pytest.mark.parametrize("shape", [(1, 2, 300, 64), (1, 1, 300, 256)])
+def test_dropout_forward_moving_maximum(shape, pattern, causal):
     # the dropout forward takes the same base decisions before zeroing the
     # dropped weights; O (scaled by 256/t) and LSE against the oracle
     from oracle import dropout as DR
-    shape, p, seed = (1, 2, 300, 64), 0.2, 0x5EED
+    p, seed = 0.2, 0x5EED
+    B, H, N, d = shape
+    scale = 1.0 / math.sqrt(d)
     q, k, v, do = make_trending_inputs(shape, torch.bfloat16, 90, pattern, 150.0)
     qd, kd, vd = (x.to(dev()) for x in (q, k, v))
-    o, lse = fa.forward_dropout(qd, kd, vd, 0.125, causal, p, seed)
+    o, lse = fa.forward_dropout(qd, kd, vd, scale, causal, p, seed)
     torch.cuda.synchronize()
     t = DR.keep_threshold(p)
-    keep = DR.keep_masks(seed, 1, 2, 300, t)
-    ro, rl = DR.attention_forward_backward_dropout(q, k, v, do, 0.125, causal, keep, t)[:2]
-    what = f"{pattern} causal={causal}"
+    keep = DR.keep_masks(seed, B, H, N, t)
+    ro, rl = DR.attention_forward_backward_dropout(q, k, v, do, scale, causal, keep, t)[:2]
+    what = f"{shape} {pattern} causal={causal}"
     assert max_abs(o.cpu(), ro) <= 2e-2 * 256 / t, f"{what}: O {max_abs(o.cpu(), ro)}"
     assert max_abs(lse.cpu(), rl) <= 1e-3, f"{what}: LSE {max_abs(lse.cpu(), rl)}"
 
