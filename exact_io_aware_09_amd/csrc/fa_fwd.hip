@@ -123,8 +123,8 @@ struct FwdCfg {
   static constexpr bool QST = QL;
   // software-pipelined loop (head dim 256 at one wavefront per SIMD, where no
   // other wavefront fills the matrix cores during a softmax)
-  static constexpr bool PIPE = D >= 256 && FA_FWD_PIPE_D256 && RB == 1 && KB == 1 && DMA_PER_TILE == 4 &&
-                               KSTEPS == 16 && PU == 2;
+  static constexpr bool PIPE = D >= 256 && FA_FWD_PIPE_D256 && RB == 1 && (KB == 1 || KB == 2) &&
+                               KSTEPS == 16 && PU == 2 * KB;
   static_assert(ST >= 2 && ST <= 3, "two or three K/V stages");
 };
 
@@ -586,7 +586,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
       // range (zeros) or rows it does not need, into a stage that is not
       // read again.
       constexpr bool spread = !first;
-      auto copy_part = [&](int i) {  // copies 0..3: K of block t+ST-1; 4..7: V of block t+ST-2
+      auto copy_part = [&](int i) {  // copies of K of block t+ST-1, then of V of block t+ST-2
         if (i < C::DMA_PER_TILE) copy_k(j0 + (ST - 1) * BC, sk, i);
         else copy_v(j0 + (ST - 2) * BC, sv, i - C::DMA_PER_TILE);
       };
@@ -597,17 +597,20 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
       if (active) {
         f32x16 sacc[RB][C::KB];
         if constexpr (spread) {
-          // S^T = K Q^T written in issue order: K fragment reads A ahead,
-          // copies between the matrix instructions
-          constexpr int A = FA_FWD_IGLP_D256 > 0 ? FA_FWD_IGLP_D256 : 3, W = A + 1;
+          // S^T = K Q^T written in issue order (the KB 32-key blocks one
+          // after the other): K fragment reads A ahead, copies between the
+          // matrix instructions
+          constexpr int A = FA_FWD_IGLP_D256 > 0 ? FA_FWD_IGLP_D256 : 3, W = A + 1, NS = C::KB * C::KSTEPS;
+          auto kread = [&](int n) { return frag_rows<D>(Ks, 32 * (n / C::KSTEPS), 16 * (n % C::KSTEPS), c32, h); };
           bf16x8 kw[W];
 #pragma unroll
-          for (int i = 0; i < A; ++i) kw[i] = frag_rows<D>(Ks, 0, 16 * i, c32, h);
+          for (int i = 0; i < A; ++i) kw[i] = kread(i);
           const f32x16 z = {};
 #pragma unroll
-          for (int i = 0; i < C::KSTEPS; ++i) {
-            if (i + A < C::KSTEPS) kw[(i + A) % W] = frag_rows<D>(Ks, 0, 16 * (i + A), c32, h);
-            sacc[0][0] = mfma32x32x16(kw[i % W], qf[0][i], i == 0 ? z : sacc[0][0]);
+          for (int i = 0; i < NS; ++i) {
+            if (i + A < NS) kw[(i + A) % W] = kread(i + A);
+            const int kb = i / C::KSTEPS, ks = i % C::KSTEPS;
+            sacc[0][kb] = mfma32x32x16(kw[i % W], qf[0][ks], ks == 0 ? z : sacc[0][kb]);
             if (i % FA_FWD_DMA_GAP == 0 && i / FA_FWD_DMA_GAP < 2 * C::DMA_PER_TILE) {
               pin();
               copy_part(i / FA_FWD_DMA_GAP);
@@ -621,8 +624,10 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
             const int kq = j0 + 4 * h - (q0w + c32);
             const int lim = CAUSAL ? min(-kq, nk - 1) : nk - 1;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (8 * (r >> 2) + (r & 3) > lim) sacc[0][0][r] = -INFINITY;
+            for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[0][kb][r] = -INFINITY;
           }
         } else {
           scores(Ks, j0, sacc);
@@ -647,10 +652,11 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                 vw[n % W] = frag_tr<D>(Vp, 16 * (n / C::DB), (n % C::DB) * 32, lane);
               }
               oacc[0][i % C::DB] = mfma32x32x16(vw[i % W], pp[i / C::DB], oacc[0][i % C::DB]);
-              sacc[0][0][i] = fast_exp2(fmaf(sacc[0][0][i], c, -mb));
+              // one exponential per matrix instruction (NV = 16 KB of them)
+              sacc[0][i / 16][i % 16] = fast_exp2(fmaf(sacc[0][i / 16][i % 16], c, -mb));
               if constexpr (spread) {
                 // the copies that did not fit in the score section
-                constexpr int NS = (C::KSTEPS + FA_FWD_DMA_GAP - 1) / FA_FWD_DMA_GAP;
+                constexpr int NS = (C::KB * C::KSTEPS + FA_FWD_DMA_GAP - 1) / FA_FWD_DMA_GAP;
                 if (NS + (i - 2) / 3 < 2 * C::DMA_PER_TILE && i >= 2 && (i - 2) % 3 == 0) {
                   pin();
                   copy_part(NS + (i - 2) / 3);
@@ -658,11 +664,14 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                 }
               }
             }
-            float part[8];
+            // row sum in the order exponentiate() takes it
+            float part[C::KB * 8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) part[r] = sacc[0][0][2 * r] + sacc[0][0][2 * r + 1];
+            for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-            for (int n = 8; n > 1; n /= 2)
+              for (int r = 0; r < 8; ++r) part[kb * 8 + r] = sacc[0][kb][2 * r] + sacc[0][kb][2 * r + 1];
+#pragma unroll
+            for (int n = C::KB * 8; n > 1; n /= 2)
 #pragma unroll
               for (int i = 0; i < n / 2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
             rs[0] = part[0];
@@ -692,22 +701,27 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                 }
               }
           }
-          sacc[0][0] = s2[0][0];
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb) sacc[0][kb] = s2[0][kb];
           rs[0] = exponentiate(sacc[0], base(m[0]));
         }
         l[0] += rs[0];
         if constexpr (DROP) {
-          uint32_t dw[4];
-          draws_query_cols(q0w, j0, bh, lane, dr.k0, dr.k1, dw);
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!kept(dw, r, dr.thresh)) sacc[0][0][r] = 0.f;
+          for (int kb = 0; kb < C::KB; ++kb) {
+            uint32_t dw[4];
+            draws_query_cols(q0w, j0 + 32 * kb, bh, lane, dr.k0, dr.k1, dw);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (!kept(dw, r, dr.thresh)) sacc[0][kb][r] = 0.f;
+          }
         }
-        // k-step u of V^T P^T: registers 8u.. of the block (keys 16u + 8*(e>>2) + 4h + (e&3))
+        // k-step u of V^T P^T: registers 8*(u&1).. of key block u>>1 (keys
+        // 16u + 8*(e>>2) + 4h + (e&3))
 #pragma unroll
         for (int u = 0; u < C::PU; ++u) {
-          const f32x16& pv_ = sacc[0][0];
-          const int r0 = 8 * u;
+          const f32x16& pv_ = sacc[0][u >> 1];
+          const int r0 = 8 * (u & 1);
           pp[u] = bf16x8_from(pack_bf16x2(pv_[r0], pv_[r0 + 1]), pack_bf16x2(pv_[r0 + 2], pv_[r0 + 3]),
                               pack_bf16x2(pv_[r0 + 4], pv_[r0 + 5]), pack_bf16x2(pv_[r0 + 6], pv_[r0 + 7]));
         }
@@ -1023,6 +1037,14 @@ hipError_t run_merge(const float* Opart, const float* Lpart, int splits, void* O
 #ifndef FA_FWD_CFG_D256
 #define FA_FWD_CFG_D256 4, 1, 32, 2, 1
 #endif
+// plain non-causal head-dim-256 forward: 64-key blocks (half the steps,
+// barriers and row-sum checks per key).  The causal, sparse, key-split and
+// dropout kernels keep 32-key blocks: with 64 their unrolled loop bodies
+// (mask and rescale paths included) outgrow the instruction cache -- the
+// causal kernel ran 15x slower.
+#ifndef FA_FWD_CFG_D256_NC
+#define FA_FWD_CFG_D256_NC 4, 1, 64, 2, 1
+#endif
 
 }  // namespace
 
@@ -1085,6 +1107,7 @@ hipError_t launch_forward_dropout_bf16_d256(const void* Q, const void* K, const 
 hipError_t launch_forward_bf16_d256(const void* Q, const void* K, const void* V, void* O,
                                     float* LSE, const Problem& p, hipStream_t stream,
                                     SparseArgs sp) {
+  if (!p.causal && !sp.on()) return run_fwd<256, FA_FWD_CFG_D256_NC, false>(Q, K, V, O, LSE, p, stream, sp);
   return run_fwd_c<256, FA_FWD_CFG_D256>(Q, K, V, O, LSE, p, stream, sp);
 }
 #endif
