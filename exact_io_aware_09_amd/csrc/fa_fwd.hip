@@ -1039,8 +1039,9 @@ hipError_t run_merge(const float* Opart, const float* Lpart, int splits, void* O
 #endif
 // plain non-causal head-dim-256 forward: 64-key blocks (half the steps,
 // barriers and row-sum checks per key).  The causal, sparse, key-split and
-// dropout kernels keep 32-key blocks: the causal kernel with 64-key blocks
-// gave the same results but ran 15x slower, and the others were not timed.
+// dropout kernels keep 32-key blocks: compiled with 64, the causal kernel
+// needs 704 bytes of scratch per lane (the registers run out) and ran 15x
+// slower.
 #ifndef FA_FWD_CFG_D256_NC
 #define FA_FWD_CFG_D256_NC 4, 1, 64, 2, 1
 #endif
