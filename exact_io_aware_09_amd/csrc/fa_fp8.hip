@@ -174,6 +174,42 @@ __device__ __forceinline__ int off8(int row, int chunk) {
   return row * RB + ((chunk ^ swz8<RB>(row)) << 4);
 }
 
+// Active forward steps at head dim 256 spread their K/V copies between the
+// score section's matrix instructions instead of issuing them at the start of
+// the step (at head dim 64 the burst measured faster)
+#ifndef FA_FP8_SPREAD
+#define FA_FP8_SPREAD 1
+#endif
+
+// lds_copy4 without the compiler memory clobber (see lds_copy16_free).
+__device__ __forceinline__ void lds_copy4_free(copy_rsrc r, uint32_t voff, uint32_t lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(r));
+}
+
+// Copy number i of dma_tile8 on its own, issued without the compiler memory
+// clobber (lds_copy16_free): for a stage nothing reads before the next ring
+// barrier.
+template <int RB, int ROWS, int NT>
+__device__ __forceinline__ void dma_tile8_part(copy_rsrc r, int r0, uint32_t gstride, uint32_t col0,
+                                               uint8_t* tile, int tid, int i) {
+  constexpr int CPR = RB / 16;
+  constexpr int NWAVE = NT / kWave;
+  const int w = tid >> 6, lane = tid & 63;
+  const int blk = w + i * NWAVE;
+  const int pos = blk * 64 + lane;
+  const int row = pos / CPR, k = (pos % CPR) ^ swz8<RB>(row);
+  lds_copy16_free(r, (uint32_t)(r0 + row) * gstride + col0 + (uint32_t)k * 16u,
+                  lds_address(tile + blk * 1024));
+}
+
 // Copy of ROWS rows of RB bytes -- global row r at byte (r0 + r) * gstride +
 // col0 -- into a swizzled tile, without VGPRs (lane L of an instruction fills
 // LDS slot 64 i + L, so it fetches the chunk the swizzle puts there).
@@ -218,6 +254,8 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   constexpr int TILE = 64 * D;
   constexpr int PER = 2 * (TILE / 16 / NT) + 1;  // copies per lane per block
+  constexpr int NKV = TILE / 16 / NT;             // copies per tile per lane
+  constexpr bool SPREAD = FA_FP8_SPREAD && D >= 256 && NKV == KS;  // one copy per S instruction
   static_assert(NW == 4, "the scale copies take one wavefront per 256 bytes");
   static_assert(ST == 2 || ST == 3, "two or three stages");
   __shared__ __attribute__((aligned(16))) uint8_t k0s[TILE], v0s[TILE], s0s[1024];
@@ -303,9 +341,32 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
 
   auto step = [&](int t, auto S) {
     constexpr int SN = (decltype(S)::value + ST - 1) % ST;  // stage of step t+ST-1
-    if (t + ST - 1 < ntiles) fetch(t + ST - 1, std::integral_constant<int, SN>{});
     const int j0 = t * BC;
     const bool active = !CAUSAL || j0 <= q0w + 31;
+    // Active steps spread their copies over the score section, one after
+    // each matrix instruction (a copy holds up its wavefront's issue until
+    // the texture unit takes it; a burst at the start of the step stalls all
+    // four wavefronts).  There they are issued unconditionally: past the last
+    // block they fetch zeros or unneeded rows into a stage not read again.
+    if (!SPREAD || !active) {
+      if (t + ST - 1 < ntiles) fetch(t + ST - 1, std::integral_constant<int, SN>{});
+    }
+    auto copy_part = [&](int i) {
+      const int j1 = (t + ST - 1) * BC;
+      __builtin_amdgcn_sched_barrier(0x406);
+      if (i < NKV) {
+        dma_tile8_part<D, 64, NT>(rk, j1, (uint32_t)D, 0u, kst(std::integral_constant<int, SN>{}), tid, i);
+      } else if (i < 2 * NKV) {
+        dma_tile8_part<64, D, NT>(rv, 0, (uint32_t)Np, (uint32_t)j1, vst(std::integral_constant<int, SN>{}), tid,
+                                  i - NKV);
+      } else {
+        const uint32_t off = wu < 2 ? (uint32_t)j1 * (D / 32) + 256u * wu
+                                    : (uint32_t)(j1 / 32) * D + 256u * (wu - 2);
+        lds_copy4_free(wu < 2 ? rks : rvs, off + 4u * lane,
+                       lds_address(sst(std::integral_constant<int, SN>{}) + 256 * wu));
+      }
+      __builtin_amdgcn_sched_barrier(0x406);
+    };
     if (active) {
       const uint8_t* Kt = kst(S);
       const uint8_t* Vt = vst(S);
@@ -321,7 +382,9 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
           const int ksc = Sc[row * (D / 32) + 2 * s + h];
           const f32x16 z = {};
           sacc[kb] = mfma_fp8(kf, qf[s], s == 0 ? z : sacc[kb], ksc, qsc[s]);
+          if constexpr (SPREAD) copy_part(kb * KS + s);
         }
+      if constexpr (SPREAD) copy_part(2 * NKV);  // the scale blocks
       const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
       if (need_mask) {
         keep_branch();
@@ -412,6 +475,9 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
       if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>{});
     }
   }
+  // the last step's copies (issued unconditionally) land before the
+  // workgroup ends
+  if constexpr (SPREAD) wait_vmem_le<0>();
 
   // O = acc / l (bf16); LSE = (m + log2 l - 8) ln 2 (l counts weights * 2^8)
   const float lt = sum_halves(l);
