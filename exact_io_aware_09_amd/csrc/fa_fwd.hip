@@ -58,11 +58,26 @@ constexpr float kMaxWeight = 65536.0f;  // bound on one lane's share of a block'
 //    runs on the matrix cores while the softmax of block t runs on the
 //    vector ALU);
 //  * FA_FWD_DMA_GAP: matrix instructions between two of a step's K/V copies.
+// Head dim 64 without the causal mask (four wavefronts per SIMD):
+//  * FA_FWD_PIPE_D64: the same pipelined loop, four exponentials per P.V
+//    matrix instruction; K fragment reads FA_FWD_PIPE_D64_KA, V fragment
+//    reads FA_FWD_PIPE_D64_VA matrix instructions ahead (longer read-ahead
+//    spills at 128 VGPRs).  The causal kernel keeps the plain loop: with
+//    the pipeline it needs more registers than four wavefronts leave.
 #ifndef FA_FWD_IGLP_D256
 #define FA_FWD_IGLP_D256 5
 #endif
 #ifndef FA_FWD_PIPE_D256
 #define FA_FWD_PIPE_D256 1
+#endif
+#ifndef FA_FWD_PIPE_D64
+#define FA_FWD_PIPE_D64 1
+#endif
+#ifndef FA_FWD_PIPE_D64_KA
+#define FA_FWD_PIPE_D64_KA 2
+#endif
+#ifndef FA_FWD_PIPE_D64_VA
+#define FA_FWD_PIPE_D64_VA 1
 #endif
 #ifndef FA_FWD_PIPE_VA
 #define FA_FWD_PIPE_VA 5
@@ -122,9 +137,11 @@ struct FwdCfg {
   static constexpr bool QL = BR * D * 2 <= 16384;
   static constexpr bool QST = QL;
   // software-pipelined loop (head dim 256 at one wavefront per SIMD, where no
-  // other wavefront fills the matrix cores during a softmax)
-  static constexpr bool PIPE = D >= 256 && FA_FWD_PIPE_D256 && RB == 1 && (KB == 1 || KB == 2) &&
-                               KSTEPS == 16 && PU == 2 * KB;
+  // other wavefront fills the matrix cores during a softmax; head dim 64,
+  // where a wavefront's own P.V then overlaps its softmax)
+  static constexpr bool PIPE = ((D >= 256 && FA_FWD_PIPE_D256 && KSTEPS == 16) ||
+                                (D == 64 && FA_FWD_PIPE_D64)) &&
+                               RB == 1 && (KB == 1 || KB == 2) && PU == 2 * KB;
   static_assert(ST >= 2 && ST <= 3, "two or three K/V stages");
 };
 
@@ -157,7 +174,9 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      SplitArgs sa = {}, SparseArgs sp = {}, DropArgs dr = {}) {
   using C = FwdCfg<D, NW, RB, BC, ST>;
   static_assert((int)SPLIT + (int)SPARSE + (int)DROP <= 1, "one variant at a time");
-  constexpr bool PIPE = C::PIPE && !SPARSE;
+  // at head dim 64 only without the causal mask: the causal kernel needs
+  // more registers than four wavefronts per SIMD leave and spills
+  constexpr bool PIPE = C::PIPE && !SPARSE && !(D == 64 && CAUSAL);
   static_assert(!SPARSE || (ST == 2 && C::BR == 128), "sparse walk: two stages, 128-row query blocks");
   // One LDS variable per stage and operand: with the stage a compile-time
   // constant at every access, the compiler can tell the block being read
@@ -600,7 +619,8 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
           // S^T = K Q^T written in issue order (the KB 32-key blocks one
           // after the other): K fragment reads A ahead, copies between the
           // matrix instructions
-          constexpr int A = FA_FWD_IGLP_D256 > 0 ? FA_FWD_IGLP_D256 : 3, W = A + 1, NS = C::KB * C::KSTEPS;
+          constexpr int A = D == 64 ? FA_FWD_PIPE_D64_KA : FA_FWD_IGLP_D256 > 0 ? FA_FWD_IGLP_D256 : 3;
+          constexpr int W = A + 1, NS = C::KB * C::KSTEPS;
           auto kread = [&](int n) { return frag_rows<D>(Ks, 32 * (n / C::KSTEPS), 16 * (n % C::KSTEPS), c32, h); };
           bf16x8 kw[W];
 #pragma unroll
@@ -639,8 +659,8 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
         } else {
           {
             // written in issue order: V fragment reads A ahead, then each
-            // matrix instruction followed by one score's exponential
-            constexpr int A = FA_FWD_PIPE_VA, NV = C::PU * C::DB, W = A + 1;
+            // matrix instruction followed by its share of the exponentials
+            constexpr int A = D == 64 ? FA_FWD_PIPE_D64_VA : FA_FWD_PIPE_VA, NV = C::PU * C::DB, W = A + 1;
             const float mb = base(m[0]);
             bf16x8 vw[W];
 #pragma unroll
@@ -652,8 +672,15 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                 vw[n % W] = frag_tr<D>(Vp, 16 * (n / C::DB), (n % C::DB) * 32, lane);
               }
               oacc[0][i % C::DB] = mfma32x32x16(vw[i % W], pp[i / C::DB], oacc[0][i % C::DB]);
-              // one exponential per matrix instruction (NV = 16 KB of them)
-              sacc[0][i / 16][i % 16] = fast_exp2(fmaf(sacc[0][i / 16][i % 16], c, -mb));
+              // the block's 16 KB exponentials spread evenly over the NV
+              // matrix instructions (one each at head dim 256)
+              constexpr int EPM = 16 * C::KB / NV;
+              static_assert(EPM * NV == 16 * C::KB, "exponentials per matrix instruction");
+#pragma unroll
+              for (int e = 0; e < EPM; ++e) {
+                const int n = i * EPM + e;
+                sacc[0][n / 16][n % 16] = fast_exp2(fmaf(sacc[0][n / 16][n % 16], c, -mb));
+              }
               if constexpr (spread) {
                 // the copies that did not fit in the score section
                 constexpr int NS = (C::KB * C::KSTEPS + FA_FWD_DMA_GAP - 1) / FA_FWD_DMA_GAP;

@@ -19,6 +19,7 @@ from exact_io_aware_09_amd import build as B
 
 D256_UNITS = [(n, f) for n, f in B.UNITS if n.endswith("_d256.hip")]
 D128NC_UNIT = [(n, f) for n, f in B.UNITS if n == "fa_bwd_d128nc.hip"]
+FWD_UNIT = [(n, f) for n, f in B.UNITS if n == "fa_fwd.hip"]
 
 
 def resource_remarks(name, extra):
@@ -75,3 +76,19 @@ def test_head_dim_128_noncausal_unit():
             assert scratch <= 32, f"{name}: {k} spills ({kernels[k]})"
         else:
             assert scratch == 0, f"{name}: {k} spills ({kernels[k]})"
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not (B.Path("/opt/rocm/bin/hipcc").exists()),
+                    reason="hipcc not available")
+def test_head_dim_64_forward_kernels_fit_four_waves():
+    # every head-dim-64 forward (plain, split, block-sparse, dropout; causal
+    # or not) keeps four wavefronts per SIMD without scratch: the non-causal
+    # ones run the software-pipelined loop, whose read-ahead is sized for that
+    (name, extra), = FWD_UNIT
+    kernels = resource_remarks(name, extra)
+    fwd = [k for k in kernels if "fwd_bf16_kernelILi64E" in k]
+    assert len(fwd) >= 7, sorted(kernels)
+    for k in fwd:
+        r = kernels[k]
+        assert r.get("ScratchSize [bytes/lane]") == 0, f"{name}: {k} spills ({r})"
+        assert r["VGPRs"] + r.get("AGPRs", 0) <= 128, f"{name}: {k} {r}"
