@@ -541,8 +541,10 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
   if constexpr (PIPE) {
     // Software pipeline.  Step t computes the scores of block t, then its
     // softmax on the vector ALU interleaved with O^T += V^T P^T of block t-1
-    // on the matrix cores (one wavefront per SIMD: nothing else would fill
-    // the matrix cores during the softmax).  Step t copies in K of block
+    // on the matrix cores (at head dim 256, one wavefront per SIMD: nothing
+    // else would fill the matrix cores during the softmax; at head dim 64 the
+    // wavefront's own P.V overlaps its softmax besides what the SIMD's other
+    // three wavefronts overlap).  Step t copies in K of block
     // t+ST-1 and V of block t+ST-2: the K ring holds blocks t..t+ST-1 and
     // the V ring blocks t-1..t+ST-2, each block in stage (block mod ST).
     // Causal steps are active up to the wavefront's diagonal and inactive
