@@ -181,6 +181,17 @@ __device__ __forceinline__ int off8(int row, int chunk) {
 #define FA_FP8_SPREAD 1
 #endif
 
+// The running maximum is raised only when a block's maximum exceeds it by
+// more than FA_FP8_LAG (log2 units).  Weights are scaled so that the running
+// maximum maps to 2^8 and E4M3 holds up to 448 = 2^8.807, so a base that
+// lags a row's largest score by at most 0.75 keeps every weight below
+// 2^8.75 < 448; the base never exceeds the row's largest score, so the row
+// sum stays >= 2^8 and a subnormal weight's rounding stays within 2^-18 of
+// the row's total.  Rows then rescale O and l far less often.
+#ifndef FA_FP8_LAG
+#define FA_FP8_LAG 0.75f
+#endif
+
 // lds_copy4 without the compiler memory clobber (see lds_copy16_free).
 __device__ __forceinline__ void lds_copy4_free(copy_rsrc r, uint32_t voff, uint32_t lds) {
   int saved;
@@ -399,14 +410,15 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
             if (koff > lim) sacc[kb][r] = -INFINITY;
           }
       }
-      // online softmax: the block's maximum (log2 units) raises m
+      // online softmax: a block's maximum (log2 units) more than FA_FP8_LAG
+      // above m raises m
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
       mx = max_halves(mx) * c;
-      if (wave_any(mx > m)) {
+      if (wave_any(mx > m + FA_FP8_LAG)) {
         keep_branch();
         const float mn = fmaxf(m, mx);
         const float alpha = fast_exp2(m - mn);  // 0 on the first block (m = -inf)
@@ -417,7 +429,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         m = mn;
       }
-      // weights * 2^8 = exp2(c s + 8 - m), in (0, 256]; row sum in fp32
+      // weights * 2^8 = exp2(c s + 8 - m), in (0, 2^8.75]; row sum in fp32
       const float bias = 8.f - m;
       float part[16];
 #pragma unroll
