@@ -107,6 +107,28 @@ def test_forward_fp8_matches_oracle(shape, seed, causal):
                        f"{shape} causal={causal} head ({b},{h})")
 
 
+@pytest.mark.parametrize("x", [1.5, 1.625, 3.0])
+def test_forward_fp8_running_maximum_lag(x):
+    # One 64-key block with score 1 at key 0, the next with score x at key
+    # 64, every other score 0 (scale 1): in log2 units the second block's
+    # maximum exceeds the first by 1.4427 (x - 1) = 0.72, 0.90 or 2.89.  The
+    # kernel raises its running maximum only past a 0.75 lag, so at 0.72 the
+    # key-64 weight is 2^8.72 = 422 (E4M3 holds 448) and at 0.90 and 2.89 the
+    # row rescales; a lag above 0.807 would overflow E4M3 at 0.90.  All values
+    # are exact in E4M3, so quantisation is exact.
+    N, d = 128, 64
+    q = torch.zeros(1, 1, N, d)
+    q[..., 0] = 1.0
+    k = torch.zeros(1, 1, N, d)
+    k[0, 0, 0, 0] = 1.0
+    k[0, 0, 64, 0] = x
+    v = make_inputs((1, 1, N, d), torch.bfloat16, 31)[2]
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    o, lse = run_fp8(q, k, v, 1.0, False)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    check_head(o[0, 0], lse[0, 0], q[0, 0], k[0, 0], v[0, 0], 1.0, False, np.arange(N), f"x={x}")
+
+
 def test_forward_fp8_spread_magnitudes():
     # per-row magnitudes over 16 binades: every block uses its own exponent
     shape = (1, 2, 256, 64)
