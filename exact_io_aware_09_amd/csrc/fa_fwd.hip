@@ -79,6 +79,12 @@ constexpr float kMaxWeight = 65536.0f;  // bound on one lane's share of a block'
 #ifndef FA_FWD_PIPE_D64_VA
 #define FA_FWD_PIPE_D64_VA 1
 #endif
+// Causal head-dim-64 forwards with N >= FA_FWD_LONG_N run the two-loop
+// kernel (LONGC): measured 1.5% faster at N = 2048, 6-8% at 8192-65536, and
+// 5% slower at N = 1024, where few blocks lie left of the diagonal.
+#ifndef FA_FWD_LONG_N
+#define FA_FWD_LONG_N 2048
+#endif
 #ifndef FA_FWD_PIPE_VA
 #define FA_FWD_PIPE_VA 5
 #endif
@@ -166,7 +172,7 @@ struct FwdCfg {
 // before it; the dropped weights are zeroed before P V, and the kept ones
 // are scaled by 256 / t in the final division.
 template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL, bool SPLIT = false,
-          bool SPARSE = false, bool DROP = false>
+          bool SPARSE = false, bool DROP = false, bool LONGC = false>
 __global__ __launch_bounds__(NW * 64, OCC)
 void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      const bf16_t* __restrict__ V, bf16_t* __restrict__ O,
@@ -174,9 +180,14 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      SplitArgs sa = {}, SparseArgs sp = {}, DropArgs dr = {}) {
   using C = FwdCfg<D, NW, RB, BC, ST>;
   static_assert((int)SPLIT + (int)SPARSE + (int)DROP <= 1, "one variant at a time");
-  // at head dim 64 only without the causal mask: the causal kernel needs
-  // more registers than four wavefronts per SIMD leave and spills
-  constexpr bool PIPE = C::PIPE && !SPARSE && !(D == 64 && CAUSAL);
+  // Causal head dim 64 with long rows (LONGC): the pipelined loop runs over
+  // the blocks left of the workgroup's diagonal only (every wavefront
+  // active, nothing masked), the plain loop over the rest; a pipelined loop
+  // that also handled waves past their diagonal would need more registers
+  // than four wavefronts leave.  Short causal rows keep the plain loop alone.
+  constexpr bool PIPE = C::PIPE && !SPARSE && (D != 64 || !CAUSAL || LONGC);
+  constexpr bool TWO = PIPE && CAUSAL && D == 64;
+  static_assert(!TWO || ST == 2, "two-loop causal forward: two stages");
   static_assert(!SPARSE || (ST == 2 && C::BR == 128), "sparse walk: two stages, 128-row query blocks");
   // One LDS variable per stage and operand: with the stage a compile-time
   // constant at every access, the compiler can tell the block being read
@@ -588,16 +599,17 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
     // keeps the matrix instructions and the copies in program order (vector
     // and scalar ALU instructions may still move across)
     auto pin = [] { __builtin_amdgcn_sched_barrier(0x406); };
-    auto pstep = [&](int t, auto S, auto FIRST) {
+    auto pstep = [&](int t, auto S, auto FIRST, auto OFFD) {
       constexpr int s = decltype(S)::value;
       constexpr bool first = decltype(FIRST)::value;
+      constexpr bool offd = decltype(OFFD)::value;  // a block left of the diagonal
       constexpr int sk = (s + ST - 1) % ST;  // stage of K(t+ST-1), and of V(t-1)
       constexpr int sv = (s + ST - 2) % ST;  // stage of V(t+ST-2)
       const int j0 = kbase + t * BC;
       const bool kf = t + ST - 1 < ntiles, vf = t + ST - 2 < ntiles;
       const bf16_t* Ks = kst(S);
       const bf16_t* Vp = vst(std::integral_constant<int, sk>{});  // V of block t-1
-      const bool active = !CAUSAL || j0 <= q0w + C::RW - 1;
+      const bool active = offd || !CAUSAL || j0 <= q0w + C::RW - 1;
       // Main path (active steps after the first): the copies are spread
       // over the score section, one after every FA_FWD_DMA_GAP-th matrix
       // instruction.  Each copy holds up the wavefront's issue until the
@@ -639,7 +651,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
               pin();
             }
           }
-          const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w);
+          const bool need_mask = !offd && ((j0 + BC > N) || (CAUSAL && j0 + BC - 1 > q0w));
           if (need_mask) {
             keep_branch();
             const int nk = N - j0 - 4 * h;
@@ -765,15 +777,42 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
       else wait_vmem_tiles<C::DMA_PER_TILE, 2>((int)kf + (int)vf);
       ring_barrier();
     };
-    pstep(0, S0{}, std::true_type{});
-    for (int t = 1; t < ntiles; t += ST) {
-      pstep(t, S1{}, std::false_type{});
-      if (t + 1 < ntiles) pstep(t + 1, S2{}, std::false_type{});
+    using OFF = std::integral_constant<bool, TWO>;
+    // blocks run by the pipelined loop: all, or those left of the diagonal
+    const int ntp = TWO ? min(ntiles, max(0, (q0 - kbase) / BC)) : ntiles;
+    if (ntp > 0) pstep(0, S0{}, std::true_type{}, OFF{});
+    for (int t = 1; t < ntp; t += ST) {
+      pstep(t, S1{}, std::false_type{}, OFF{});
+      if (t + 1 < ntp) pstep(t + 1, S2{}, std::false_type{}, OFF{});
       if constexpr (ST > 2) {
-        if (t + 2 < ntiles) pstep(t + 2, S0{}, std::false_type{});
+        if (t + 2 < ntp) pstep(t + 2, S0{}, std::false_type{}, OFF{});
       }
     }
-    if (pend) {
+    if (TWO && ntp < ntiles) {
+      // Hand over to the plain loop at block ntp: its K came in during the
+      // last pipelined step (or before the loop); copy its V into the stage
+      // of its parity (which held block ntp-2's), add block ntp-1's pending
+      // product, and let the plain loop go on from there.
+      const int jn = kbase + ntp * BC;
+      if ((ntp & 1) == 0) dma_tile<D, BC, C::NT>(rv, jn, v0s, tid);
+      else dma_tile<D, BC, C::NT>(rv, jn, v1s, tid);
+      if (pend) {
+        if ((ntp & 1) == 0) pv(v1s);
+        else pv(v0s);
+        pend = false;
+      }
+      wait_vmem_le<0>();
+      ring_barrier();
+      int t = ntp;
+      if (t & 1) {
+        step(t, jn, -1, std::integral_constant<int, 1>{});
+        ++t;
+      }
+      for (; t < ntiles; t += 2) {
+        step(t, kbase + t * BC, -1, std::integral_constant<int, 0>{});
+        if (t + 1 < ntiles) step(t + 1, kbase + (t + 1) * BC, -1, std::integral_constant<int, 1>{});
+      }
+    } else if (pend) {
       // P.V of the last block
       const int sl = (ntiles - 1) % ST;
       if (sl == 0) {
@@ -926,10 +965,15 @@ hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* 
                          (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, sp);
     else
       return hipErrorNotSupported;
-  } else
+  } else if (CAUSAL && D == 64 && C::PIPE && p.N >= FA_FWD_LONG_N) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, false, false, true>),
+                       dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
+                       (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{});
+  } else {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid),
                        dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                        (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{});
+  }
   return hipGetLastError();
 }
 

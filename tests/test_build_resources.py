@@ -82,13 +82,20 @@ def test_head_dim_128_noncausal_unit():
                     reason="hipcc not available")
 def test_head_dim_64_forward_kernels_fit_four_waves():
     # every head-dim-64 forward (plain, split, block-sparse, dropout; causal
-    # or not) keeps four wavefronts per SIMD without scratch: the non-causal
-    # ones run the software-pipelined loop, whose read-ahead is sized for that
+    # or not) keeps four wavefronts per SIMD, and all but one without
+    # scratch: the non-causal ones run the software-pipelined loop, whose
+    # read-ahead is sized for that.  The causal long-row kernel (last
+    # template flag set: pipelined loop left of the diagonal, plain loop on
+    # it) keeps both loops' state and spills a few bytes per lane; it is
+    # still the faster one from N = 2048 on, so it may use at most 32.
     (name, extra), = FWD_UNIT
     kernels = resource_remarks(name, extra)
     fwd = [k for k in kernels if "fwd_bf16_kernelILi64E" in k]
-    assert len(fwd) >= 7, sorted(kernels)
+    assert len(fwd) >= 8, sorted(kernels)
+    longc = [k for k in fwd if re.search(r"ELb1ELb0ELb0ELb0ELb1E", k)]
+    assert len(longc) == 1, fwd
     for k in fwd:
         r = kernels[k]
-        assert r.get("ScratchSize [bytes/lane]") == 0, f"{name}: {k} spills ({r})"
+        limit = 32 if k in longc else 0
+        assert r.get("ScratchSize [bytes/lane]") <= limit, f"{name}: {k} spills ({r})"
         assert r["VGPRs"] + r.get("AGPRs", 0) <= 128, f"{name}: {k} {r}"

@@ -119,6 +119,14 @@ def test_bf16_shapes(shape, causal):
     full_case(shape, torch.bfloat16, causal, seed=sum(shape) + 17, mult=0.5 if shape[3] == 256 else 1.0)
 
 
+# Causal rows long enough for the two-loop head-dim-64 forward (pipelined
+# left of each query block's diagonal, plain on it; N >= 2048), with an odd
+# and an even number of blocks before the diagonal and ragged tails.
+@pytest.mark.parametrize("shape", [(1, 2, 2048, 64), (1, 1, 2100, 64), (1, 1, 3000, 64)])
+def test_bf16_long_causal_rows(shape):
+    full_case(shape, torch.bfloat16, True, seed=sum(shape) + 19, mult=1.0)
+
+
 # --------------------------------------------------------------------------
 # GPT-2-medium attention shape, full tensors, checked 8 batches at a time
 @pytest.fixture(scope="module")
