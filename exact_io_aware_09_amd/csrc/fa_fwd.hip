@@ -36,6 +36,10 @@
 //    weight) is redone with its own maximum and O, l rescaled, as in the
 //    pages' update.  Rows decide individually, so each row's arithmetic
 //    depends on its own scores alone.
+//  * Software-pipelined loop (head dim 256; head dim 64 without the causal
+//    mask, and, for causal rows of 2048 keys or more, over the blocks left of
+//    each query block's diagonal): the P.V product of block t-1 runs
+//    interleaved with the softmax of block t, K copied one block ahead of V.
 //  * Workgroups are remapped so that all query blocks of a head run on one
 //    XCD (shared L2 for the re-read K/V); within a group of heads that fills
 //    an XCD, the longest causal blocks of every head start first.
