@@ -25,10 +25,12 @@
 //
 // Forward kernel: the second version's loop order (one block of 128 query
 // rows per workgroup, loop over blocks of 64 keys, O divided once at the
-// end), with the plain online softmax of the pages (a block's maximum raises
-// the running maximum, O and l are rescaled).  The weights enter P V as E4M3
-// after scaling by 2^8 (e^(s - m) * 256 lies in (0, 256], so small weights
-// keep 2^-17 of resolution); the row sum is taken in fp32 before rounding.
+// end), with the online softmax of the pages (a block's maximum raises the
+// running maximum, O and l are rescaled), except that the running maximum
+// is raised only when a block's maximum exceeds it by more than FA_FP8_LAG.
+// The weights enter P V as E4M3 after scaling by 2^8 (e^(s - m) * 256 lies
+// in (0, 2^8.75], so small weights keep 2^-17 of resolution relative to the
+// row sum); the row sum is taken in fp32 before rounding.
 #include <type_traits>
 
 #include "fa_device.h"
