@@ -84,7 +84,7 @@ constexpr float kMaxWeight = 65536.0f;  // bound on one lane's share of a block'
 #define FA_FWD_PIPE_D64_VA 1
 #endif
 // Causal head-dim-64 forwards with N >= FA_FWD_LONG_N run the two-loop
-// kernel (LONGC): measured 1.5% faster at N = 2048, 6-8% at 8192-65536, and
+// kernel (NOMASK): measured 1.5% faster at N = 2048, 6-8% at 8192-65536, and
 // 5% slower at N = 1024, where few blocks lie left of the diagonal.
 #ifndef FA_FWD_LONG_N
 #define FA_FWD_LONG_N 2048
@@ -176,7 +176,7 @@ struct FwdCfg {
 // before it; the dropped weights are zeroed before P V, and the kept ones
 // are scaled by 256 / t in the final division.
 template <int D, int NW, int RB, int BC, int ST, int OCC, bool CAUSAL, bool SPLIT = false,
-          bool SPARSE = false, bool DROP = false, bool LONGC = false>
+          bool SPARSE = false, bool DROP = false, bool NOMASK = false>
 __global__ __launch_bounds__(NW * 64, OCC)
 void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      const bf16_t* __restrict__ V, bf16_t* __restrict__ O,
@@ -184,13 +184,17 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
                      SplitArgs sa = {}, SparseArgs sp = {}, DropArgs dr = {}) {
   using C = FwdCfg<D, NW, RB, BC, ST>;
   static_assert((int)SPLIT + (int)SPARSE + (int)DROP <= 1, "one variant at a time");
-  // Causal head dim 64 with long rows (LONGC): the pipelined loop runs over
-  // the blocks left of the workgroup's diagonal only (every wavefront
-  // active, nothing masked), the plain loop over the rest; a pipelined loop
-  // that also handled waves past their diagonal would need more registers
-  // than four wavefronts leave.  Short causal rows keep the plain loop alone.
-  constexpr bool PIPE = C::PIPE && !SPARSE && (D != 64 || !CAUSAL || LONGC);
+  // NOMASK (chosen by the launcher): the pipelined loop carries no mask.
+  // Causal head dim 64 with long rows: it runs over the blocks left of the
+  // workgroup's diagonal only (every wavefront active, nothing masked), the
+  // plain loop over the rest; a pipelined loop that also handled waves past
+  // their diagonal would need more registers than four wavefronts leave, so
+  // short causal rows keep the plain loop alone.  Without the causal mask
+  // (head dim 256): N is a multiple of the block size, so no block has a
+  // tail.
+  constexpr bool PIPE = C::PIPE && !SPARSE && (D != 64 || !CAUSAL || NOMASK);
   constexpr bool TWO = PIPE && CAUSAL && D == 64;
+  static_assert(!NOMASK || !CAUSAL || TWO, "no mask: causal only for the two-loop kernel");
   static_assert(!TWO || ST == 2, "two-loop causal forward: two stages");
   static_assert(!SPARSE || (ST == 2 && C::BR == 128), "sparse walk: two stages, 128-row query blocks");
   // One LDS variable per stage and operand: with the stage a compile-time
@@ -781,7 +785,7 @@ void fwd_bf16_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
       else wait_vmem_tiles<C::DMA_PER_TILE, 2>((int)kf + (int)vf);
       ring_barrier();
     };
-    using OFF = std::integral_constant<bool, TWO>;
+    using OFF = std::integral_constant<bool, TWO || (NOMASK && !CAUSAL)>;
     // blocks run by the pipelined loop: all, or those left of the diagonal
     const int ntp = TWO ? min(ntiles, max(0, (q0 - kbase) / BC)) : ntiles;
     if (ntp > 0) pstep(0, S0{}, std::true_type{}, OFF{});
@@ -969,11 +973,20 @@ hipError_t run_fwd(const void* Q, const void* K, const void* V, void* O, float* 
                          (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, sp);
     else
       return hipErrorNotSupported;
-  } else if (CAUSAL && D == 64 && C::PIPE && p.N >= FA_FWD_LONG_N) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, false, false, true>),
-                       dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
-                       (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{});
   } else {
+    // the unmasked pipelined loop: causal head dim 64 with long rows, or head
+    // dim 256 without the causal mask and without a partial block (0.8%
+    // faster at 2·16·16384·256; neutral at head dim 64, which keeps one kernel)
+    constexpr bool can = C::PIPE && (CAUSAL ? D == 64 : D >= 256);
+    if constexpr (can) {
+      if (CAUSAL ? p.N >= FA_FWD_LONG_N : p.N % BC == 0) {
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, false, false, true>),
+                           dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q,
+                           (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c,
+                           SplitArgs{}, SparseArgs{});
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL>), dim3((unsigned)grid),
                        dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                        (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{});

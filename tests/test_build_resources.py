@@ -84,10 +84,10 @@ def test_head_dim_64_forward_kernels_fit_four_waves():
     # every head-dim-64 forward (plain, split, block-sparse, dropout; causal
     # or not) keeps four wavefronts per SIMD, and all but one without
     # scratch: the non-causal ones run the software-pipelined loop, whose
-    # read-ahead is sized for that.  The causal long-row kernel (last
-    # template flag set: pipelined loop left of the diagonal, plain loop on
-    # it) keeps both loops' state and spills a few bytes per lane; it is
-    # still the faster one from N = 2048 on, so it may use at most 32.
+    # read-ahead is sized for that.  The causal long-row kernel (causal and
+    # the last template flag set: pipelined loop left of the diagonal, plain
+    # loop on it) keeps both loops' state and spills a few bytes per lane; it
+    # is still the faster one from N = 2048 on, so it may use at most 32.
     (name, extra), = FWD_UNIT
     kernels = resource_remarks(name, extra)
     fwd = [k for k in kernels if "fwd_bf16_kernelILi64E" in k]

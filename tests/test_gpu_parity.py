@@ -127,6 +127,13 @@ def test_bf16_long_causal_rows(shape):
     full_case(shape, torch.bfloat16, True, seed=sum(shape) + 19, mult=1.0)
 
 
+# No causal mask and N a multiple of the key-block size (32 keys at head dim
+# 64, 64 at head dim 256): the forward's pipelined loop without mask code.
+@pytest.mark.parametrize("shape", [(1, 2, 256, 64), (2, 1, 1024, 64), (1, 1, 512, 256), (1, 1, 1024, 256)])
+def test_bf16_unmasked_blocks(shape):
+    full_case(shape, torch.bfloat16, False, seed=sum(shape) + 23, mult=0.5 if shape[3] == 256 else 1.0)
+
+
 # --------------------------------------------------------------------------
 # GPT-2-medium attention shape, full tensors, checked 8 batches at a time
 @pytest.fixture(scope="module")
