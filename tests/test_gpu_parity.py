@@ -223,6 +223,18 @@ def test_bitwise_deterministic():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("shape,causal", [((1, 4, 4096, 64), True), ((1, 2, 2048, 256), False)])
+def test_bitwise_deterministic_other_forward_loops(shape, causal):
+    # the two-loop causal forward for long rows, the head-dim-256 forward
+    # without mask code: the same bits on every run
+    B, H, N, d = shape
+    inp = make_inputs(shape, torch.bfloat16, 12, 0.5 if d == 256 else 1.0)
+    a = run_gpu(*inp, d ** -0.5, causal)
+    b = run_gpu(*inp, d ** -0.5, causal)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_causal_rows_ignore_future_on_gpu(dtype):
     q, k, v, do = make_inputs((2, 2, 700, 64), dtype, 21)
