@@ -85,7 +85,9 @@ constexpr float kMaxWeight = 65536.0f;  // bound on one lane's share of a block'
 #endif
 // Causal head-dim-64 forwards with N >= FA_FWD_LONG_N run the two-loop
 // kernel (NOMASK): measured 1.5% faster at N = 2048, 6-8% at 8192-65536, and
-// 5% slower at N = 1024, where few blocks lie left of the diagonal.
+// 5% slower at N = 1024, where few blocks lie left of the diagonal.  The
+// split-KV and dropout forwards follow the same rule (at N = 65536: 7% and
+// 2.4% faster).
 #ifndef FA_FWD_LONG_N
 #define FA_FWD_LONG_N 2048
 #endif
@@ -1004,6 +1006,15 @@ hipError_t run_fwd_drop(const void* Q, const void* K, const void* V, void* O, fl
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = p.scale * kLog2e;
   const int G = head_group(OCC * 4 / NW, nqb);
+  if constexpr (CAUSAL && D == 64 && C::PIPE) {
+    if (p.N >= FA_FWD_LONG_N) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, false, true, true>),
+                         dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q,
+                         (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c,
+                         SplitArgs{}, SparseArgs{}, dr);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, false, false, true>),
                      dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K,
                      (const bf16_t*)V, (bf16_t*)O, LSE, BH, p.N, nqb, G, c, SplitArgs{}, SparseArgs{},
@@ -1086,6 +1097,15 @@ hipError_t run_fwd_split(const void* Q, const void* K, const void* V, const Prob
   sa.splits = splits;
   sa.Opart = Opart;
   sa.Lpart = Lpart;
+  if constexpr (CAUSAL && D == 64 && C::PIPE) {
+    if (p.N >= FA_FWD_LONG_N) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, true, false, false, true>),
+                         dim3((unsigned)grid), dim3(C::NT), 0, stream, (const bf16_t*)Q,
+                         (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)nullptr, (float*)nullptr, BH,
+                         p.N, nqb, G, c, sa);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, RB, BC, ST, OCC, CAUSAL, true>), dim3((unsigned)grid),
                      dim3(C::NT), 0, stream, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
                      (bf16_t*)nullptr, (float*)nullptr, BH, p.N, nqb, G, c, sa);

@@ -82,20 +82,22 @@ def test_head_dim_128_noncausal_unit():
                     reason="hipcc not available")
 def test_head_dim_64_forward_kernels_fit_four_waves():
     # every head-dim-64 forward (plain, split, block-sparse, dropout; causal
-    # or not) keeps four wavefronts per SIMD, and all but one without
+    # or not) keeps four wavefronts per SIMD, and all but three without
     # scratch: the non-causal ones run the software-pipelined loop, whose
-    # read-ahead is sized for that.  The causal long-row kernel (causal and
+    # read-ahead is sized for that.  The causal long-row kernels (causal and
     # the last template flag set: pipelined loop left of the diagonal, plain
-    # loop on it) keeps both loops' state and spills a few bytes per lane; it
-    # is still the faster one from N = 2048 on, so it may use at most 32.
+    # loop on it; plain, split and dropout) keep both loops' state and spill
+    # a few bytes per lane; they are still the faster ones from N = 2048 on,
+    # so they may use at most 40.
     (name, extra), = FWD_UNIT
     kernels = resource_remarks(name, extra)
     fwd = [k for k in kernels if "fwd_bf16_kernelILi64E" in k]
     assert len(fwd) >= 8, sorted(kernels)
-    longc = [k for k in fwd if re.search(r"ELb1ELb0ELb0ELb0ELb1E", k)]
-    assert len(longc) == 1, fwd
+    # template flags after OCC: CAUSAL, SPLIT, SPARSE, DROPOUT, and the last one
+    longc = [k for k in fwd if re.search(r"ELb1ELb[01]ELb0ELb[01]ELb1E", k)]
+    assert len(longc) == 3, fwd
     for k in fwd:
         r = kernels[k]
-        limit = 32 if k in longc else 0
+        limit = 40 if k in longc else 0
         assert r.get("ScratchSize [bytes/lane]") <= limit, f"{name}: {k} spills ({r})"
         assert r["VGPRs"] + r.get("AGPRs", 0) <= 128, f"{name}: {k} {r}"

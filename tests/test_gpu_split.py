@@ -59,7 +59,11 @@ def split_raw(q, k, v, scale, causal, splits):
 
 SPLIT_CASES = [((1, 2, 300, 64), 2), ((1, 2, 300, 64), 3), ((2, 1, 1000, 64), 7),
                ((1, 1, 77, 64), 2), ((1, 1, 100, 64), 8), ((1, 1, 129, 128), 3),
-               ((1, 2, 520, 256), 4), ((1, 1, 1, 64), 4)]
+               ((1, 2, 520, 256), 4), ((1, 1, 1, 64), 4),
+               # rows of 2048 keys and more: with the causal mask the head-dim-64
+               # kernel runs the blocks left of each query block's diagonal
+               # without mask code, range by range
+               ((1, 1, 2100, 64), 3), ((1, 2, 4096, 64), 2)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
